@@ -1,0 +1,229 @@
+// C ABI of libfp8sm.so: argument validation, scale sizing, shape dispatch and
+// launch.  Every check runs on the host before anything is enqueued, and the
+// kernel that runs is exactly the one validated -- no silent fallback (the
+// load-time / run-time gate mismatch described in the prhub digest of sglang
+// PR #33148, implementation section, is the failure this avoids).
+#include <hip/hip_runtime_api.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "../../include/fp8sm.h"
+#include "launch.h"
+#include "dispatch_table.h"
+
+using namespace fp8sm;
+
+namespace {
+
+std::atomic<int> g_forced_variant{-1};
+
+// gfx950 check, cached per device id.
+fp8sm_status check_device() {
+  static std::mutex mu;
+  static signed char ok_cache[64];
+  static bool init = false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8SM_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return FP8SM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!init) {
+    memset(ok_cache, -1, sizeof ok_cache);
+    init = true;
+  }
+  if (ok_cache[dev] < 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FP8SM_ERR_DEVICE;
+    ok_cache[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  }
+  return ok_cache[dev] ? FP8SM_OK : FP8SM_ERR_DEVICE;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline fp8sm_status launched(hipError_t e) { return e == hipSuccess ? FP8SM_OK : FP8SM_ERR_LAUNCH; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxK = 65536;
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8sm_status_str(fp8sm_status s) {
+  switch (s) {
+    case FP8SM_OK: return "ok";
+    case FP8SM_ERR_NULL: return "null pointer argument";
+    case FP8SM_ERR_SHAPE: return "invalid shape, leading dimension or group size";
+    case FP8SM_ERR_ALIGN: return "pointer, leading dimension or size breaks the 16-byte alignment rule";
+    case FP8SM_ERR_UNSUPPORTED: return "unsupported enum value or combination";
+    case FP8SM_ERR_LAUNCH: return "kernel launch failed";
+    case FP8SM_ERR_DEVICE: return "current device is not gfx950 (MI355X) or unavailable";
+    case FP8SM_ERR_RANGE: return "size beyond the supported range";
+    default: return "unknown status";
+  }
+}
+
+size_t fp8sm_scale_bytes(fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, int64_t M, int64_t K_out,
+                         int32_t group) {
+  if (M < 0 || K_out <= 0 || group <= 0 || K_out % group) return 0;
+  if (fmt != FP8SM_SCALE_FP32 && fmt != FP8SM_SCALE_UE8M0_FP32 && fmt != FP8SM_SCALE_UE8M0_BYTE)
+    return 0;
+  if (lay != FP8SM_LAYOUT_ROW_MAJOR && lay != FP8SM_LAYOUT_MN_MAJOR) return 0;
+  const int64_t G = K_out / group;
+  const int64_t esz = fmt == FP8SM_SCALE_UE8M0_BYTE ? 1 : 4;
+  const int64_t rows = lay == FP8SM_LAYOUT_MN_MAJOR ? ((M + 3) / 4) * 4 : M;
+  return (size_t)(rows * G * esz);
+}
+
+fp8sm_status fp8sm_quant_group(const void* x, fp8sm_dtype in, int64_t M, int64_t K_out,
+                               int64_t ld_x, int32_t group, uint32_t flags,
+                               fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, uint8_t* q,
+                               int64_t ld_q, void* scales, hipStream_t stream) {
+  if (in != FP8SM_BF16 && in != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;
+  if (fmt != FP8SM_SCALE_FP32 && fmt != FP8SM_SCALE_UE8M0_FP32 && fmt != FP8SM_SCALE_UE8M0_BYTE)
+    return FP8SM_ERR_UNSUPPORTED;
+  if (lay != FP8SM_LAYOUT_ROW_MAJOR && lay != FP8SM_LAYOUT_MN_MAJOR) return FP8SM_ERR_UNSUPPORTED;
+  if (flags & ~FP8SM_FUSE_SILU_MUL) return FP8SM_ERR_UNSUPPORTED;
+  const bool fused = (flags & FP8SM_FUSE_SILU_MUL) != 0;
+  if (M < 0 || K_out <= 0) return FP8SM_ERR_SHAPE;
+  if (M > kMaxDim || K_out > kMaxDim) return FP8SM_ERR_RANGE;
+  if (group != 128 && group != K_out) return FP8SM_ERR_SHAPE;
+  if (K_out % group) return FP8SM_ERR_SHAPE;
+  const int64_t row_in = fused ? 2 * K_out : K_out;
+  if (ld_x < row_in || ld_q < K_out) return FP8SM_ERR_SHAPE;
+  if (K_out % 8 || ld_x % 8 || ld_q % 8) return FP8SM_ERR_ALIGN;
+  if (M == 0) return FP8SM_OK;
+  if (!x || !q || !scales) return FP8SM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scales, fmt == FP8SM_SCALE_UE8M0_BYTE ? 1 : 4))
+    return FP8SM_ERR_ALIGN;
+  fp8sm_status st = check_device();
+  if (st != FP8SM_OK) return st;
+  QuantArgs a;
+  a.x = x;
+  a.f16 = in == FP8SM_FP16;
+  a.M = M;
+  a.K = K_out;
+  a.ld_x = ld_x;
+  a.group = group;
+  a.fused = fused;
+  a.fmt = (int)fmt;
+  a.mn_major = lay == FP8SM_LAYOUT_MN_MAJOR;
+  a.mpad = ((M + 3) / 4) * 4;
+  a.q = q;
+  a.ld_q = ld_q;
+  a.scales = scales;
+  return launched(launch_quant_group(a, stream));
+}
+
+fp8sm_status fp8sm_quant_static(const void* x, fp8sm_dtype in, int64_t M, int64_t K,
+                                int64_t ld_x, const float* scale, uint8_t* q, int64_t ld_q,
+                                hipStream_t stream) {
+  if (in != FP8SM_BF16 && in != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;
+  if (M < 0 || K <= 0) return FP8SM_ERR_SHAPE;
+  if (M > kMaxDim || K > kMaxDim) return FP8SM_ERR_RANGE;
+  if (ld_x < K || ld_q < K) return FP8SM_ERR_SHAPE;
+  if (K % 8 || ld_x % 8 || ld_q % 8) return FP8SM_ERR_ALIGN;
+  if (M == 0) return FP8SM_OK;
+  if (!x || !q || !scale) return FP8SM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 4)) return FP8SM_ERR_ALIGN;
+  fp8sm_status st = check_device();
+  if (st != FP8SM_OK) return st;
+  return launched(launch_quant_static(x, in == FP8SM_FP16, M, K, ld_x, scale, q, ld_q, stream));
+}
+
+fp8sm_status fp8sm_quant_weight_block128(const void* w, fp8sm_dtype in, int64_t N, int64_t K,
+                                         int64_t ld_w, uint8_t* q, int64_t ld_q, float* scales,
+                                         hipStream_t stream) {
+  if (in != FP8SM_BF16 && in != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;
+  if (N < 0 || K <= 0) return FP8SM_ERR_SHAPE;
+  if (N > kMaxDim || K > kMaxDim || (N + 127) / 128 > 65535) return FP8SM_ERR_RANGE;
+  if (ld_w < K || ld_q < K) return FP8SM_ERR_SHAPE;
+  if (K % 8 || ld_w % 8 || ld_q % 8) return FP8SM_ERR_ALIGN;
+  if (N == 0) return FP8SM_OK;
+  if (!w || !q || !scales) return FP8SM_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(q, 8) || !aligned(scales, 4)) return FP8SM_ERR_ALIGN;
+  fp8sm_status st = check_device();
+  if (st != FP8SM_OK) return st;
+  return launched(launch_quant_wblock(w, in == FP8SM_FP16, N, K, ld_w, q, ld_q, scales, stream));
+}
+
+fp8sm_status fp8sm_silu_mul_f32(const void* x, fp8sm_dtype in, int64_t M, int64_t K_out,
+                                int64_t ld_x, float* y, int64_t ld_y, hipStream_t stream) {
+  if (in != FP8SM_BF16 && in != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;
+  if (M < 0 || K_out <= 0) return FP8SM_ERR_SHAPE;
+  if (M > kMaxDim || K_out > kMaxDim) return FP8SM_ERR_RANGE;
+  if (ld_x < 2 * K_out || ld_y < K_out) return FP8SM_ERR_SHAPE;
+  if (K_out % 8 || ld_x % 8 || ld_y % 8) return FP8SM_ERR_ALIGN;
+  if (M == 0) return FP8SM_OK;
+  if (!x || !y) return FP8SM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return FP8SM_ERR_ALIGN;
+  fp8sm_status st = check_device();
+  if (st != FP8SM_OK) return st;
+  return launched(launch_silu_mul(x, in == FP8SM_FP16, M, K_out, ld_x, y, ld_y, stream));
+}
+
+int fp8sm_variant_count(void) { return VAR_COUNT; }
+
+const char* fp8sm_variant_name(int id) { return variant_name(id); }
+
+int fp8sm_force_variant(int id) {
+  if (id < -1 || id >= VAR_COUNT) id = -1;
+  return g_forced_variant.exchange(id);
+}
+
+int fp8sm_pick_variant(int64_t M, int64_t N, int64_t K) {
+  const int forced = g_forced_variant.load();
+  if (forced >= 0) return forced;
+  return pick_from_table(M, N, K);
+}
+
+fp8sm_status fp8sm_scaled_mm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                             void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                             fp8sm_scale_kind ka, const void* sa, fp8sm_scale_kind kb,
+                             const void* sb, hipStream_t stream) {
+  const bool rowwise = (ka == FP8SM_KIND_TENSOR || ka == FP8SM_KIND_ROW) &&
+                       (kb == FP8SM_KIND_TENSOR || kb == FP8SM_KIND_COL);
+  const bool blockwise = (ka == FP8SM_KIND_GROUP128_UE8M0 || ka == FP8SM_KIND_GROUP128_FP32) &&
+                         kb == FP8SM_KIND_BLOCK128;
+  if (!rowwise && !blockwise) return FP8SM_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0) return FP8SM_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxK) return FP8SM_ERR_RANGE;
+  if (lda < K || ldb < K || ldc < N) return FP8SM_ERR_SHAPE;
+  if (K % 16 || lda % 16 || ldb % 16) return FP8SM_ERR_ALIGN;
+  if (N % 8 || ldc % 8) return FP8SM_ERR_ALIGN;
+  if (M == 0 || N == 0) return FP8SM_OK;
+  if (!C) return FP8SM_ERR_NULL;
+  if (!aligned(C, 16)) return FP8SM_ERR_ALIGN;
+  if (K > 0) {
+    if (!A || !B || !sa || !sb) return FP8SM_ERR_NULL;
+    if (!aligned(A, 16) || !aligned(B, 16)) return FP8SM_ERR_ALIGN;
+    if (!aligned(sb, 4) || (ka != FP8SM_KIND_GROUP128_UE8M0 && !aligned(sa, 4)))
+      return FP8SM_ERR_ALIGN;
+  }
+  fp8sm_status st = check_device();
+  if (st != FP8SM_OK) return st;
+  uint16_t* Cb = static_cast<uint16_t*>(C);
+  if (K == 0) return launched(launch_fill_zero_bf16(Cb, ldc, M, N, stream));
+  GemmArgs g;
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.C = Cb;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.sa = sa;
+  g.sa_kind = (int)ka;
+  g.sb = sb;
+  g.sb_kind = (int)kb;
+  if (blockwise) return launched(launch_gemm_blockwise(g, stream));
+  int v = fp8sm_pick_variant(M, N, K);
+  if (!variant_accepts(v, M)) return FP8SM_ERR_UNSUPPORTED;
+  return launched(launch_gemm_rowwise(v, g, stream));
+}
+
+}  // extern "C"

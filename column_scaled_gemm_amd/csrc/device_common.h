@@ -1,0 +1,78 @@
+// Device helpers shared by the fp8sm kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8sm {
+
+constexpr float kQMax = 448.0f;        // largest finite E4M3FN magnitude
+constexpr float kAmaxFloor = 1e-10f;   // group absmax floor (a compile-time constant)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (data read once: no reuse expected in the caches).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Exact widening of eight packed 16-bit inputs (one 16-byte load) to fp32.
+template <bool F16>
+__device__ __forceinline__ void widen8(const uint4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (F16) {
+      f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+      f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    } else {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+// silu(g) = RN32(g / RN32(1 + E)), E the correctly rounded fp32 e^-g.  E is
+// evaluated as the fp64 exponential rounded to fp32; the parity tests check
+// exhaustively that this is the correctly rounded value for every gate value
+// a bf16 or fp16 input can hold.  The divide is the IEEE fp32 divide.
+__device__ __forceinline__ float silu_f32(float g) {
+  const float e = (float)exp(-(double)g);
+  const float d = 1.0f + e;
+  return g / d;
+}
+
+// Clamp to the E4M3FN range and convert eight fp32 values to codes
+// (round to nearest even, sign of zero kept).  The hardware conversion does
+// not saturate, so the clamp comes first.
+__device__ __forceinline__ uint2 to_e4m3_x8(const float* v) {
+  float c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(v[i], -kQMax), kQMax);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// ceil(log2 s) for a positive normal fp32 s, from its bit fields.
+__device__ __forceinline__ int ue8m0_exponent(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return (int)((b >> 23) & 0xFFu) - 127 + ((b & 0x7FFFFFu) != 0u ? 1 : 0);
+}
+__device__ __forceinline__ float pow2f(int e) {  // 2^e, -126 <= e <= 127
+  return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = WIDTH / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace fp8sm

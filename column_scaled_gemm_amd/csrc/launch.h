@@ -1,0 +1,60 @@
+// Internal launcher interface between the C-ABI layer (api.cpp) and the
+// kernels (quant.hip, gemm.hip).  Host code only; no HIP device code here.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fp8sm {
+
+struct QuantArgs {
+  const void* x;
+  bool f16;
+  int64_t M, K, ld_x;
+  int64_t group;  // 128 or K
+  bool fused;
+  int fmt;        // 0 fp32, 1 ue8m0 as fp32, 2 ue8m0 byte
+  int mn_major;
+  int64_t mpad;
+  uint8_t* q;
+  int64_t ld_q;
+  void* scales;
+};
+
+hipError_t launch_quant_group(const QuantArgs& a, hipStream_t s);
+hipError_t launch_quant_static(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x,
+                               const float* scale, uint8_t* q, int64_t ld_q, hipStream_t s);
+hipError_t launch_silu_mul(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x, float* y,
+                           int64_t ld_y, hipStream_t s);
+hipError_t launch_quant_wblock(const void* w, bool f16, int64_t N, int64_t K, int64_t ld_w,
+                               uint8_t* q, int64_t ld_q, float* scales, hipStream_t s);
+
+struct GemmArgs {
+  const uint8_t* A;
+  int64_t lda;
+  const uint8_t* B;
+  int64_t ldb;
+  uint16_t* C;
+  int64_t ldc;
+  int64_t M, N, K;
+  const void* sa;
+  int sa_kind;  // fp8sm_scale_kind
+  const void* sb;
+  int sb_kind;
+};
+
+// Rowwise / per-tensor variants.  All of them produce bitwise-identical rows.
+enum Variant {
+  VAR_TILE_256x128 = 0,  // large tiles, LDS-staged, 4 wavefronts of 128x64
+  VAR_TILE_128x128 = 1,  // medium tiles, 4 wavefronts of 64x64
+  VAR_DECODE_16 = 2,     // M <= 16: split-K across wavefronts, in-order merge
+  VAR_DECODE_32 = 3,     // M <= 32
+  VAR_DECODE_64 = 4,     // M <= 64
+  VAR_COUNT = 5
+};
+const char* variant_name(int v);
+bool variant_accepts(int v, int64_t M);
+hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_blockwise(const GemmArgs& g, hipStream_t s);
+hipError_t launch_fill_zero_bf16(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s);
+
+}  // namespace fp8sm

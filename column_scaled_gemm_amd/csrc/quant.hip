@@ -1,0 +1,433 @@
+// Activation / weight quantization kernels to OCP E4M3FN (gfx950).
+//
+// Group rule (sglang PR #33533 "[JIT] per_token_group_quant: fix the fp16
+// UE8M0 multiplier overflow ...", commit messages and Motivation): for each
+// group, a' = max(max|y|, 1e-10), s = RN32(a'/448); fp32 scales quantize with
+// the correctly rounded multiplier RN32(448/a'), UE8M0 scales with 2^-e,
+// e = ceil(log2 s).  Every multiply is fp32, whatever the input dtype, so the
+// fp16 multiplier overflow of that PR's Modifications 1 cannot occur.
+// Fused SiLU-and-mul follows Modifications 2 (silu per element, plain divide).
+//
+// Memory layout: x row-major [M][ld_x] bf16/fp16 (a fused row is [gate|up]),
+// codes row-major [M][ld_q], scales row-major [M][G] or group-major
+// [G][M_pad].  Every kernel reads each input element once from HBM with
+// 16-byte loads that are contiguous across a wavefront, and writes codes with
+// 8-byte stores that are contiguous across the wavefront.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8sm {
+
+enum { FMT_FP32 = 0, FMT_UE8M0_FP32 = 1, FMT_UE8M0_BYTE = 2 };
+
+template <int FMT>
+__device__ __forceinline__ float group_multiplier(float amax, float* scale_val, int* ebyte) {
+  const float a = fmaxf(amax, kAmaxFloor);
+  const float s = a / kQMax;
+  if constexpr (FMT == FMT_FP32) {
+    *scale_val = s;
+    *ebyte = 0;
+    return kQMax / a;
+  } else {
+    const int e = ue8m0_exponent(s);
+    *scale_val = pow2f(e);
+    *ebyte = e + 127;
+    return pow2f(-e);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_scale(void* scales, int64_t idx, float v, int ebyte) {
+  if constexpr (FMT == FMT_UE8M0_BYTE) {
+    static_cast<uint8_t*>(scales)[idx] = (uint8_t)ebyte;
+  } else {
+    static_cast<float*>(scales)[idx] = v;
+  }
+}
+
+template <bool F16, bool FUSED>
+__device__ __forceinline__ void load_values(const uint4 gv, const uint4 uv, float* y) {
+  widen8<F16>(gv, y);
+  if constexpr (FUSED) {
+    float u[8];
+    widen8<F16>(uv, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = silu_f32(y[i]) * u[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 groups.  A 16-lane quarter of a wavefront owns one group (16 lanes x 8
+// values); a wavefront owns kQuads x 4 consecutive groups of the flattened
+// (row, group) index, issuing all its loads before any arithmetic.
+template <bool F16, bool FUSED, int FMT>
+__global__ __launch_bounds__(256) void quant_g128_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t G, int64_t K, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, int mn_major,
+    int64_t mpad) {
+  constexpr int kQuads = 4;
+  const int lane = threadIdx.x & 63;
+  const int quarter = lane >> 4;
+  const int l16 = lane & 15;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t total = M * G;
+  uint4 gv[kQuads], uv[kQuads];
+  int64_t row[kQuads], grp[kQuads];
+#pragma unroll
+  for (int u = 0; u < kQuads; ++u) {
+    const int64_t gid = (wave * kQuads + u) * 4 + quarter;
+    row[u] = -1;
+    gv[u] = make_uint4(0, 0, 0, 0);
+    uv[u] = make_uint4(0, 0, 0, 0);
+    if (gid < total) {
+      row[u] = gid / G;
+      grp[u] = gid - row[u] * G;
+      const uint16_t* src = x + row[u] * ld_x + grp[u] * 128 + l16 * 8;
+      gv[u] = load_stream16(src);
+      if constexpr (FUSED) uv[u] = load_stream16(src + K);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kQuads; ++u) {
+    float y[8];
+    load_values<F16, FUSED>(gv[u], uv[u], y);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    amax = group_max<16>(amax);
+    float sval;
+    int eb;
+    const float mult = group_multiplier<FMT>(amax, &sval, &eb);
+    if (row[u] >= 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = y[i] * mult;
+      *reinterpret_cast<uint2*>(q + row[u] * ld_q + grp[u] * 128 + l16 * 8) = to_e4m3_x8(y);
+      if (l16 == 0) {
+        const int64_t idx = mn_major ? grp[u] * mpad + row[u] : row[u] * G + grp[u];
+        store_scale<FMT>(scales, idx, sval, eb);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per token, row kept in registers: one wavefront per row, NC 16-byte chunks
+// per lane (the host picks the smallest NC with 64 * NC * 8 >= K).
+template <bool F16, int NC, int FMT>
+__global__ __launch_bounds__(256) void quant_token_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;  // whole wavefront; the kernel has no barrier
+  const int64_t nch = K >> 3;
+  const uint16_t* xr = x + row * ld_x;
+  uint4 v[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int64_t c = lane + 64 * i;
+    v[i] = c < nch ? load_stream16(xr + c * 8)
+                   : make_uint4(0, 0, 0, 0);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    float y[8];
+    widen8<F16>(v[i], y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(y[j]));
+  }
+  amax = group_max<64>(amax);
+  float sval;
+  int eb;
+  const float mult = group_multiplier<FMT>(amax, &sval, &eb);
+  uint8_t* qr = q + row * ld_q;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int64_t c = lane + 64 * i;
+    if (c < nch) {
+      float y[8];
+      widen8<F16>(v[i], y);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
+      *reinterpret_cast<uint2*>(qr + c * 8) = to_e4m3_x8(y);
+    }
+  }
+  if (lane == 0) store_scale<FMT>(scales, row, sval, eb);
+}
+
+// Per token, any K and the fused form: two passes over the row (the second
+// pass re-reads it from L2) so no register budget limits K.
+template <bool F16, bool FUSED, int FMT>
+__global__ __launch_bounds__(256) void quant_token_2pass_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int64_t nch = K >> 3;
+  const uint16_t* xr = x + row * ld_x;
+  float amax = 0.0f;
+  for (int64_t c = lane; c < nch; c += 64) {
+    const uint4 g = *reinterpret_cast<const uint4*>(xr + c * 8);
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if constexpr (FUSED) u = *reinterpret_cast<const uint4*>(xr + K + c * 8);
+    float y[8];
+    load_values<F16, FUSED>(g, u, y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(y[j]));
+  }
+  amax = group_max<64>(amax);
+  float sval;
+  int eb;
+  const float mult = group_multiplier<FMT>(amax, &sval, &eb);
+  uint8_t* qr = q + row * ld_q;
+  for (int64_t c = lane; c < nch; c += 64) {
+    const uint4 g = *reinterpret_cast<const uint4*>(xr + c * 8);
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if constexpr (FUSED) u = *reinterpret_cast<const uint4*>(xr + K + c * 8);
+    float y[8];
+    load_values<F16, FUSED>(g, u, y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
+    *reinterpret_cast<uint2*>(qr + c * 8) = to_e4m3_x8(y);
+  }
+  if (lane == 0) store_scale<FMT>(scales, row, sval, eb);
+}
+
+// ---------------------------------------------------------------------------
+// Static per-tensor quant: q = E4M3(clamp(RN32(x * RN32(1/s)))).  Each thread
+// converts one 16-byte chunk (8 values) of the flattened (row, chunk) space.
+template <bool F16>
+__global__ __launch_bounds__(256) void quant_static_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
+    const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ld_q) {
+  const int64_t nch = K >> 3;
+  const int64_t total = M * nch;
+  const float inv = 1.0f / scale[0];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nch, c = i - r * nch;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + r * ld_x + c * 8);
+    float y[8];
+    widen8<F16>(v, y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = y[j] * inv;
+    *reinterpret_cast<uint2*>(q + r * ld_q + c * 8) = to_e4m3_x8(y);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The fused product alone in fp32 (same silu_f32 as the fused quant).
+template <bool F16>
+__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                       int64_t K, int64_t ld_x,
+                                                       float* __restrict__ y, int64_t ld_y) {
+  const int64_t nch = K >> 3;
+  const int64_t total = M * nch;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nch, c = i - r * nch;
+    const uint16_t* src = x + r * ld_x + c * 8;
+    float v[8];
+    load_values<F16, true>(*reinterpret_cast<const uint4*>(src),
+                           *reinterpret_cast<const uint4*>(src + K), v);
+    float4* dst = reinterpret_cast<float4*>(y + r * ld_y + c * 8);
+    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks: one workgroup (4 wavefronts) per block; each thread
+// holds 8 chunks of 8 values; the block maximum is reduced across the
+// workgroup through LDS.
+template <bool F16>
+__global__ __launch_bounds__(256) void quant_wblock_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ld_w,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scales, int64_t KB) {
+  __shared__ float red[4];
+  const int64_t nb = blockIdx.y, kb = blockIdx.x;
+  const int t = threadIdx.x;
+  uint4 v[8];
+  bool ok[8];
+  int64_t rr[8], cc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = t + 256 * i;         // 0..2047: 128 rows x 16 chunks
+    rr[i] = nb * 128 + (idx >> 4);
+    cc[i] = kb * 128 + (idx & 15) * 8;
+    ok[i] = rr[i] < N && cc[i] < K;
+    v[i] = ok[i] ? *reinterpret_cast<const uint4*>(w + rr[i] * ld_w + cc[i]) : make_uint4(0, 0, 0, 0);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float y[8];
+    widen8<F16>(v[i], y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(y[j]));
+  }
+  amax = group_max<64>(amax);
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float sval;
+  int eb;
+  const float mult = group_multiplier<FMT_FP32>(amax, &sval, &eb);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (ok[i]) {
+      float y[8];
+      widen8<F16>(v[i], y);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
+      *reinterpret_cast<uint2*>(q + rr[i] * ld_q + cc[i]) = to_e4m3_x8(y);
+    }
+  }
+  if (t == 0) scales[nb * KB + kb] = sval;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers
+
+template <bool F16, bool FUSED>
+static hipError_t launch_g128_fmt(int fmt, const QuantArgs& a, hipStream_t s) {
+  const int64_t G = a.K / 128;
+  const int64_t waves = (a.M * G + 15) / 16;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  switch (fmt) {
+    case FMT_FP32:
+      hipLaunchKernelGGL((quant_g128_kernel<F16, FUSED, FMT_FP32>), grid, block, 0, s, x, a.M, G,
+                         a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad);
+      break;
+    case FMT_UE8M0_FP32:
+      hipLaunchKernelGGL((quant_g128_kernel<F16, FUSED, FMT_UE8M0_FP32>), grid, block, 0, s, x,
+                         a.M, G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad);
+      break;
+    default:
+      hipLaunchKernelGGL((quant_g128_kernel<F16, FUSED, FMT_UE8M0_BYTE>), grid, block, 0, s, x,
+                         a.M, G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <bool F16, int NC>
+static hipError_t launch_token_nc(int fmt, const QuantArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.M + 3) / 4)), block(256);
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  switch (fmt) {
+    case FMT_FP32:
+      hipLaunchKernelGGL((quant_token_kernel<F16, NC, FMT_FP32>), grid, block, 0, s, x, a.M, a.K,
+                         a.ld_x, a.q, a.ld_q, a.scales);
+      break;
+    case FMT_UE8M0_FP32:
+      hipLaunchKernelGGL((quant_token_kernel<F16, NC, FMT_UE8M0_FP32>), grid, block, 0, s, x, a.M,
+                         a.K, a.ld_x, a.q, a.ld_q, a.scales);
+      break;
+    default:
+      hipLaunchKernelGGL((quant_token_kernel<F16, NC, FMT_UE8M0_BYTE>), grid, block, 0, s, x, a.M,
+                         a.K, a.ld_x, a.q, a.ld_q, a.scales);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <bool F16, bool FUSED>
+static hipError_t launch_token_2pass(int fmt, const QuantArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.M + 3) / 4)), block(256);
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  switch (fmt) {
+    case FMT_FP32:
+      hipLaunchKernelGGL((quant_token_2pass_kernel<F16, FUSED, FMT_FP32>), grid, block, 0, s, x,
+                         a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+      break;
+    case FMT_UE8M0_FP32:
+      hipLaunchKernelGGL((quant_token_2pass_kernel<F16, FUSED, FMT_UE8M0_FP32>), grid, block, 0,
+                         s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+      break;
+    default:
+      hipLaunchKernelGGL((quant_token_2pass_kernel<F16, FUSED, FMT_UE8M0_BYTE>), grid, block, 0,
+                         s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <bool F16>
+static hipError_t launch_token(int fmt, const QuantArgs& a, hipStream_t s) {
+  const int64_t per_lane = (a.K / 8 + 63) / 64;
+  if (per_lane <= 1) return launch_token_nc<F16, 1>(fmt, a, s);
+  if (per_lane <= 2) return launch_token_nc<F16, 2>(fmt, a, s);
+  if (per_lane <= 4) return launch_token_nc<F16, 4>(fmt, a, s);
+  if (per_lane <= 8) return launch_token_nc<F16, 8>(fmt, a, s);
+  if (per_lane <= 12) return launch_token_nc<F16, 12>(fmt, a, s);
+  if (per_lane <= 16) return launch_token_nc<F16, 16>(fmt, a, s);
+  if (per_lane <= 24) return launch_token_nc<F16, 24>(fmt, a, s);
+  if (per_lane <= 32) return launch_token_nc<F16, 32>(fmt, a, s);
+  return launch_token_2pass<F16, false>(fmt, a, s);
+}
+
+hipError_t launch_quant_group(const QuantArgs& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  const bool per_token = a.group == a.K;
+  if (per_token) {
+    if (a.fused) return a.f16 ? launch_token_2pass<true, true>(a.fmt, a, s)
+                              : launch_token_2pass<false, true>(a.fmt, a, s);
+    return a.f16 ? launch_token<true>(a.fmt, a, s) : launch_token<false>(a.fmt, a, s);
+  }
+  if (a.fused) return a.f16 ? launch_g128_fmt<true, true>(a.fmt, a, s)
+                            : launch_g128_fmt<false, true>(a.fmt, a, s);
+  return a.f16 ? launch_g128_fmt<true, false>(a.fmt, a, s)
+               : launch_g128_fmt<false, false>(a.fmt, a, s);
+}
+
+hipError_t launch_quant_static(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x,
+                               const float* scale, uint8_t* q, int64_t ld_q, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int64_t chunks = M * (K / 8);
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  const uint16_t* xx = static_cast<const uint16_t*>(x);
+  if (f16)
+    hipLaunchKernelGGL((quant_static_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, xx,
+                       M, K, ld_x, scale, q, ld_q);
+  else
+    hipLaunchKernelGGL((quant_static_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, xx,
+                       M, K, ld_x, scale, q, ld_q);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x, float* y,
+                           int64_t ld_y, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  int64_t blocks = (M * (K / 8) + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  const uint16_t* xx = static_cast<const uint16_t*>(x);
+  if (f16)
+    hipLaunchKernelGGL((silu_mul_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, xx, M, K,
+                       ld_x, y, ld_y);
+  else
+    hipLaunchKernelGGL((silu_mul_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, xx, M,
+                       K, ld_x, y, ld_y);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_wblock(const void* w, bool f16, int64_t N, int64_t K, int64_t ld_w,
+                               uint8_t* q, int64_t ld_q, float* scales, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  const int64_t NB = (N + 127) / 128, KB = (K + 127) / 128;
+  const dim3 grid((unsigned)KB, (unsigned)NB), block(256);
+  const uint16_t* ww = static_cast<const uint16_t*>(w);
+  if (f16)
+    hipLaunchKernelGGL((quant_wblock_kernel<true>), grid, block, 0, s, ww, N, K, ld_w, q, ld_q,
+                       scales, KB);
+  else
+    hipLaunchKernelGGL((quant_wblock_kernel<false>), grid, block, 0, s, ww, N, K, ld_w, q, ld_q,
+                       scales, KB);
+  return hipGetLastError();
+}
+
+}  // namespace fp8sm

@@ -1,0 +1,195 @@
+"""Thin ctypes binding of libfp8sm.so (the C ABI declared in include/fp8sm.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors are torch device tensors (torch provides device memory and the
+current stream); outputs are either passed in or allocated here with
+torch.empty.  The library is loaded on first use; if it is missing or fails to
+load, every call raises -- there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8sm.so")
+
+OK = 0
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPORTED",
+          5: "ERR_LAUNCH", 6: "ERR_DEVICE", 7: "ERR_RANGE"}
+
+BF16, FP16 = 0, 1
+SCALE_FP32, SCALE_UE8M0_FP32, SCALE_UE8M0_BYTE = 0, 1, 2
+LAYOUT_ROW_MAJOR, LAYOUT_MN_MAJOR = 0, 1
+KIND_TENSOR, KIND_ROW, KIND_COL = 0, 1, 2
+KIND_GROUP128_UE8M0, KIND_GROUP128_FP32, KIND_BLOCK128 = 3, 4, 5
+FUSE_SILU_MUL = 1
+
+# Every symbol include/fp8sm.h declares, with (restype, argtypes).
+_i64, _i32, _u32, _p = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p
+_int = ctypes.c_int
+SIGNATURES = {
+    "fp8sm_quant_group": (_int, [_p, _int, _i64, _i64, _i64, _i32, _u32, _int, _int, _p, _i64, _p, _p]),
+    "fp8sm_quant_static": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i64, _p]),
+    "fp8sm_quant_weight_block128": (_int, [_p, _int, _i64, _i64, _i64, _p, _i64, _p, _p]),
+    "fp8sm_scaled_mm": (_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _int, _p, _int, _p, _p]),
+    "fp8sm_silu_mul_f32": (_int, [_p, _int, _i64, _i64, _i64, _p, _i64, _p]),
+    "fp8sm_scale_bytes": (ctypes.c_size_t, [_int, _int, _i64, _i64, _i32]),
+    "fp8sm_status_str": (ctypes.c_char_p, [_int]),
+    "fp8sm_force_variant": (_int, [_int]),
+    "fp8sm_variant_count": (_int, []),
+    "fp8sm_variant_name": (ctypes.c_char_p, [_int]),
+    "fp8sm_pick_variant": (_int, [_i64, _i64, _i64]),
+}
+
+_lib = None
+
+
+class Fp8smError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _load().fp8sm_status_str(status).decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({msg})")
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "python -m column_scaled_gemm_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def lib():
+    return _load()
+
+
+def _check(status, where):
+    if status != OK:
+        raise Fp8smError(status, where)
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float16:
+        return FP16
+    raise TypeError("activations must be bfloat16 or float16")
+
+
+# ---------------------------------------------------------------- raw calls
+
+def scale_bytes(fmt, layout, M, K_out, group):
+    return _load().fp8sm_scale_bytes(fmt, layout, M, K_out, group)
+
+
+def status_str(status):
+    return _load().fp8sm_status_str(status).decode()
+
+
+def force_variant(vid):
+    return _load().fp8sm_force_variant(vid)
+
+
+def variant_count():
+    return _load().fp8sm_variant_count()
+
+
+def variant_name(vid):
+    return _load().fp8sm_variant_name(vid).decode()
+
+
+def pick_variant(M, N, K):
+    return _load().fp8sm_pick_variant(M, N, K)
+
+
+# ---------------------------------------------------------------- tensor calls
+
+def scale_shape(fmt, layout, M, K_out, group):
+    G = K_out // group
+    rows = ((M + 3) // 4) * 4 if layout == LAYOUT_MN_MAJOR else M
+    return (G, rows) if layout == LAYOUT_MN_MAJOR else (M, G)
+
+
+def quant_group(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul=False,
+                q=None, scales=None, stream=None):
+    """x [M, K_in] bf16/fp16 (K_in = 2*K_out when fused) -> (codes uint8 [M, K_out], scales)."""
+    M, K_in = x.shape
+    K_out = K_in // 2 if fuse_silu_mul else K_in
+    if group == -1:
+        group = K_out
+    if q is None:
+        q = torch.empty((M, K_out), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        dt = torch.uint8 if fmt == SCALE_UE8M0_BYTE else torch.float32
+        scales = torch.empty(scale_shape(fmt, layout, M, K_out, group), dtype=dt, device=x.device)
+    st = _load().fp8sm_quant_group(_ptr(x), _dtype_code(x), M, K_out, x.stride(0), group,
+                                   FUSE_SILU_MUL if fuse_silu_mul else 0, fmt, layout,
+                                   _ptr(q), q.stride(0), _ptr(scales), _stream(stream))
+    _check(st, "fp8sm_quant_group")
+    return q, scales
+
+
+def quant_static(x, scale, q=None, stream=None):
+    """x [M, K] bf16/fp16, scale: 1-element fp32 device tensor -> codes [M, K]."""
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    st = _load().fp8sm_quant_static(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(scale),
+                                    _ptr(q), q.stride(0), _stream(stream))
+    _check(st, "fp8sm_quant_static")
+    return q
+
+
+def quant_weight_block128(w, q=None, scales=None, stream=None):
+    N, K = w.shape
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(((N + 127) // 128, (K + 127) // 128), dtype=torch.float32,
+                             device=w.device)
+    st = _load().fp8sm_quant_weight_block128(_ptr(w), _dtype_code(w), N, K, w.stride(0), _ptr(q),
+                                             q.stride(0), _ptr(scales), _stream(stream))
+    _check(st, "fp8sm_quant_weight_block128")
+    return q, scales
+
+
+def silu_mul_f32(x, y=None, stream=None):
+    """x [M, 2K] bf16/fp16 [gate | up] -> y [M, K] fp32 = silu(gate) * up."""
+    M, K2 = x.shape
+    K = K2 // 2
+    if y is None:
+        y = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    st = _load().fp8sm_silu_mul_f32(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(y),
+                                    y.stride(0), _stream(stream))
+    _check(st, "fp8sm_silu_mul_f32")
+    return y
+
+
+def scaled_mm(a, b, sa, sb, kind_a, kind_b, c=None, M=None, stream=None):
+    """a [M, K] uint8, b [N, K] uint8 (E4M3FN codes) -> c [M, N] bf16."""
+    Mx, K = a.shape
+    M = Mx if M is None else M
+    N = b.shape[0]
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=b.device)
+    st = _load().fp8sm_scaled_mm(_ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(c), c.stride(0),
+                                 M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb), _stream(stream))
+    _check(st, "fp8sm_scaled_mm")
+    return c

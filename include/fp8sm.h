@@ -1,0 +1,199 @@
+/*
+ * fp8sm -- FP8 (E4M3FN) activation quant + scaled GEMM for MI355X (gfx950).
+ *
+ * C ABI of libfp8sm.so.  Every pointer argument named x, q, A, B, C, scale(s),
+ * sa, sb is a DEVICE pointer owned by the caller; the library allocates no
+ * device memory, never synchronizes, and enqueues its kernels on the caller's
+ * stream.  Results are valid once that stream has run them.  All arguments are
+ * validated on the host before anything is launched; a non-OK status means
+ * nothing was enqueued.  The library never aborts or throws.
+ *
+ * Pages cited (by title and section):
+ *  [P1] sglang PR #34318 "Route large SM90 row/column-scaled FP8 GEMMs to Torch"
+ *  [P2] sglang PR #44861 (SM12x deterministic static-FP8 linears)
+ *  [P3] prhub digest of sglang PR #33148 (SM90 per-tensor FP8 -> FlashInfer)
+ *  [P4] sglang PR #33533 "[JIT] per_token_group_quant: fix the fp16 UE8M0
+ *       multiplier overflow, 1.23x on the fused EP-MoE path, unify the scale
+ *       allocation"
+ *
+ * Number format: OCP FP8 E4M3FN codes, one byte each (max 448, no infinities,
+ * 0x7F / 0xFF are NaN) -- the input type required in [P1] Summary.  gfx950
+ * converts to and from this format natively; the gfx94x FNUZ variant that
+ * [P4] Modifications 3 warns about is not supported.
+ */
+#ifndef FP8SM_H
+#define FP8SM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8SM_OK = 0,
+  FP8SM_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  FP8SM_ERR_SHAPE = 2,       /* negative/zero size, ld < row length, bad group */
+  FP8SM_ERR_ALIGN = 3,       /* a pointer, leading dimension or size breaks the
+                                16-byte alignment rule of the call             */
+  FP8SM_ERR_UNSUPPORTED = 4, /* enum value or combination not supported        */
+  FP8SM_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch       */
+  FP8SM_ERR_DEVICE = 6,      /* current device is not gfx950, or no device     */
+  FP8SM_ERR_RANGE = 7        /* size beyond what the call supports             */
+} fp8sm_status;
+
+typedef enum { FP8SM_BF16 = 0, FP8SM_FP16 = 1 } fp8sm_dtype;
+
+/* Scale rounding and storage ([P4] Modifications 3: rounding, storage and
+ * layout are three separate choices, named explicitly by the caller).       */
+typedef enum {
+  FP8SM_SCALE_FP32 = 0,        /* s = RN32(amax / 448), stored as float      */
+  FP8SM_SCALE_UE8M0_FP32 = 1,  /* 2^ceil(log2 s), stored as float            */
+  FP8SM_SCALE_UE8M0_BYTE = 2   /* same power of two, stored as the biased
+                                  exponent byte e + 127                      */
+} fp8sm_scale_fmt;
+
+typedef enum {
+  FP8SM_LAYOUT_ROW_MAJOR = 0,  /* scales[m * G + g]                          */
+  FP8SM_LAYOUT_MN_MAJOR = 1    /* scales[g * M_pad + m], M_pad = M rounded up
+                                  to a multiple of 4 (group-major, the layout
+                                  a grouped consumer reads column by column) */
+} fp8sm_scale_layout;
+
+/* Scale kinds of the GEMM operands. */
+typedef enum {
+  FP8SM_KIND_TENSOR = 0,          /* one fp32 scalar (device pointer)          */
+  FP8SM_KIND_ROW = 1,             /* A: fp32 [M], one per row (per token)      */
+  FP8SM_KIND_COL = 2,             /* B: fp32 [N], one per output channel       */
+  FP8SM_KIND_GROUP128_UE8M0 = 3,  /* A: uint8 [M][ceil(K/128)] biased exponents
+                                     (scale 2^(byte-127)) per 1x128 group     */
+  FP8SM_KIND_GROUP128_FP32 = 4,   /* A: fp32 [M][ceil(K/128)] per 1x128 group  */
+  FP8SM_KIND_BLOCK128 = 5         /* B: fp32 [ceil(N/128)][ceil(K/128)] per
+                                     128x128 weight block                      */
+} fp8sm_scale_kind;
+
+#define FP8SM_FUSE_SILU_MUL 0x1u
+
+/*
+ * Per-token or per-1x128-group activation quant ([P4] commit messages and
+ * Motivation; the fused form of Modifications 2; the UE8M0 overflow fix of
+ * Modifications 1).  For each group of `group` consecutive outputs of a row:
+ *   a' = max(max|y|, 1e-10);  s = RN32(a'/448)
+ *   FP32 scales:   q = E4M3(clamp(RN32(y * RN32(448/a')), +-448))
+ *   UE8M0 scales:  e = ceil(log2 s), q = E4M3(clamp(RN32(y * 2^-e), +-448))
+ * with E4M3 round-to-nearest-even.  All scaling is done in fp32 whatever the
+ * input dtype, so no multiplier can overflow (the fp16 failure of [P4]).
+ *
+ *   x      device, bf16 or fp16 (`in`), row-major, M rows, row stride ld_x
+ *          elements.  Without FUSE_SILU_MUL a row holds K_out values y.  With
+ *          FUSE_SILU_MUL a row holds 2*K_out values [gate | up] and
+ *          y = RN32(silu(gate) * up), silu(g) = RN32(g / RN32(1 + e^-g)) with
+ *          e^-g the correctly rounded fp32 exponential.
+ *   M      rows, >= 0 (0: nothing is launched).
+ *   K_out  output columns, > 0, multiple of 8.
+ *   ld_x   >= K_out (2*K_out when fused), multiple of 8; x 16-byte aligned.
+ *   group  128 (K_out a multiple of 128) or K_out (per token).
+ *   flags  0 or FP8SM_FUSE_SILU_MUL.
+ *   fmt, lay  scale format and layout (see above).
+ *   q      device uint8 [M][ld_q] codes; ld_q >= K_out, multiple of 8;
+ *          q 8-byte aligned.
+ *   scales device, fp8sm_scale_bytes(fmt, lay, M, K_out, group) bytes.
+ * Errors: NULL pointers -> ERR_NULL; sizes -> ERR_SHAPE; alignment ->
+ * ERR_ALIGN; unknown enums -> ERR_UNSUPPORTED; non-gfx950 -> ERR_DEVICE.
+ */
+fp8sm_status fp8sm_quant_group(const void* x, fp8sm_dtype in, int64_t M, int64_t K_out,
+                               int64_t ld_x, int32_t group, uint32_t flags,
+                               fp8sm_scale_fmt fmt, fp8sm_scale_layout lay,
+                               uint8_t* q, int64_t ld_q, void* scales, hipStream_t stream);
+
+/*
+ * Static per-tensor quant with a checkpoint scale ([P3] motivation and key
+ * source excerpts: one scalar activation scale per layer):
+ *   q = E4M3(clamp(RN32(x * RN32(1/s)), +-448)).
+ *   scale  device pointer to one positive fp32 s.
+ * Shapes/alignment as fp8sm_quant_group without groups (K multiple of 8).
+ */
+fp8sm_status fp8sm_quant_static(const void* x, fp8sm_dtype in, int64_t M, int64_t K,
+                                int64_t ld_x, const float* scale, uint8_t* q, int64_t ld_q,
+                                hipStream_t stream);
+
+/*
+ * Weight quant per 128x128 block (the weight side of the blockwise GEMM):
+ * for each block, a' = max(max|w|, 1e-10), s = RN32(a'/448),
+ * q = E4M3(clamp(RN32(w * RN32(448/a')))).  w: device bf16/fp16 [N][ld_w];
+ * q: uint8 [N][ld_q]; scales: fp32 [ceil(N/128)][ceil(K/128)].
+ * K multiple of 8, ld_w / ld_q multiples of 8, w 16-byte aligned.
+ */
+fp8sm_status fp8sm_quant_weight_block128(const void* w, fp8sm_dtype in, int64_t N, int64_t K,
+                                         int64_t ld_w, uint8_t* q, int64_t ld_q, float* scales,
+                                         hipStream_t stream);
+
+/*
+ * Scaled FP8 GEMM, bf16 output, no bias ([P1] Summary: E4M3FN inputs, fp32
+ * row/column scales, bf16 output; [P3] key source excerpts: the per-tensor
+ * form with two scalar scales):
+ *   rowwise / per-tensor:  C[m,n] = bf16( acc[m,n] * sa[m] * sb[n] )
+ *   blockwise:             C[m,n] = bf16( sum_kb sa[m,kb] * sb[n/128,kb] * P_kb[m,n] )
+ * acc / P_kb are the sums over k (over one 128-wide k block) of
+ * dec(A[m,k]) * dec(B[n,k]).  Every product and sum is taken in at least
+ * fp32 precision (fp8 operands are widened exactly before the matrix cores),
+ * and the reduction order over k is fixed: row m of C depends only on row m of
+ * A, B and the scales -- not on M, on the other rows, or on which kernel
+ * variant the shape dispatch picked ([P2] Motivation and the reviewers'
+ * row-variance check).
+ *
+ *   A   device uint8 [M][lda] E4M3FN, K contiguous.
+ *   B   device uint8 [N][ldb] E4M3FN, K contiguous (the [K, N] column-major
+ *       weight of [P3]'s excerpt).
+ *   C   device bf16 [M][ldc].
+ *   ka/sa, kb/sb  scale kinds and device pointers.  Supported pairs:
+ *       {TENSOR, ROW} x {TENSOR, COL}, and {GROUP128_UE8M0, GROUP128_FP32} x
+ *       {BLOCK128}.
+ * Rules ([P3] implementation section and review: fp8 rows need 16-byte
+ * alignment, K % 16, and bf16 output rows N % 8): K % 16 == 0, lda, ldb % 16
+ * == 0, A, B 16-byte aligned; N % 8 == 0, ldc % 8 == 0, C 16-byte aligned;
+ * M, N >= 0 (0: nothing launched); K >= 0 (K == 0 writes zeros);
+ * K <= 65536.  Violations return an error status; there is no fallback path.
+ */
+fp8sm_status fp8sm_scaled_mm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                             void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                             fp8sm_scale_kind ka, const void* sa, fp8sm_scale_kind kb,
+                             const void* sb, hipStream_t stream);
+
+/*
+ * The fused product alone, in fp32: y[m][k] = RN32(silu(x[m][k]) * x[m][K_out+k])
+ * with the same silu as fp8sm_quant_group's FUSE_SILU_MUL ([P4] Modifications
+ * 2).  x: device bf16/fp16 [M][ld_x], ld_x >= 2*K_out; y: device fp32
+ * [M][ld_y].  K_out, ld_x, ld_y multiples of 8; x 16-byte, y 16-byte aligned.
+ */
+fp8sm_status fp8sm_silu_mul_f32(const void* x, fp8sm_dtype in, int64_t M, int64_t K_out,
+                                int64_t ld_x, float* y, int64_t ld_y, hipStream_t stream);
+
+/* Bytes needed for the scales of fp8sm_quant_group (0 on invalid input). */
+size_t fp8sm_scale_bytes(fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, int64_t M, int64_t K_out,
+                         int32_t group);
+
+/* Static description of a status code. */
+const char* fp8sm_status_str(fp8sm_status status);
+
+/*
+ * Test hook: force fp8sm_scaled_mm's rowwise/per-tensor dispatch to kernel
+ * variant `id` (see fp8sm_variant_name), or -1 for the measured table.
+ * Returns the previous setting.  Used to check that rows are bitwise identical
+ * whichever variant computes them.  Not thread-safe; process-wide.
+ */
+int fp8sm_force_variant(int id);
+
+/* Number of rowwise/per-tensor GEMM variants, and a name for each. */
+int fp8sm_variant_count(void);
+const char* fp8sm_variant_name(int id);
+
+/* Variant the dispatch table picks for a shape (no launch, no validation). */
+int fp8sm_pick_variant(int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8SM_H */

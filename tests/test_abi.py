@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every symbol include/fp8sm.h declares, and
+rejects bad arguments on the host before touching a device (no compute calls:
+these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+LIB = os.path.join(ROOT, "column_scaled_gemm_amd", "libfp8sm.so")
+HEADER = os.path.join(ROOT, "include", "fp8sm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libfp8sm.so not built")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8sm_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    from column_scaled_gemm_amd import fp8sm
+    lib = ctypes.CDLL(LIB)
+    names = _declared()
+    assert "fp8sm_scaled_mm" in names and "fp8sm_quant_group" in names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in fp8sm.SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings_and_scale_bytes():
+    from column_scaled_gemm_amd import fp8sm
+    assert fp8sm.status_str(0) == "ok"
+    assert "alignment" in fp8sm.status_str(3)
+    assert fp8sm.scale_bytes(fp8sm.SCALE_FP32, fp8sm.LAYOUT_ROW_MAJOR, 10, 512, 128) == 10 * 4 * 4
+    assert fp8sm.scale_bytes(fp8sm.SCALE_UE8M0_BYTE, fp8sm.LAYOUT_ROW_MAJOR, 10, 512, 128) == 40
+    assert fp8sm.scale_bytes(fp8sm.SCALE_UE8M0_BYTE, fp8sm.LAYOUT_MN_MAJOR, 10, 512, 128) == 12 * 4
+    assert fp8sm.scale_bytes(fp8sm.SCALE_FP32, fp8sm.LAYOUT_ROW_MAJOR, 10, 512, 512) == 40
+    assert fp8sm.scale_bytes(fp8sm.SCALE_FP32, fp8sm.LAYOUT_ROW_MAJOR, 10, 500, 128) == 0
+
+
+def _mm(lib, **kw):
+    a = dict(A=16, lda=512, B=16, ldb=512, C=16, ldc=256, M=64, N=256, K=512, ka=1, sa=16, kb=2,
+             sb=16)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return lib.fp8sm_scaled_mm(P(a["A"]), a["lda"], P(a["B"]), a["ldb"], P(a["C"]), a["ldc"],
+                               a["M"], a["N"], a["K"], a["ka"], P(a["sa"]), a["kb"], P(a["sb"]),
+                               P(0))
+
+
+def test_scaled_mm_rejects_bad_arguments_before_any_launch():
+    from column_scaled_gemm_amd import fp8sm
+    lib = fp8sm.lib()
+    E = {v: k for k, v in fp8sm.STATUS.items()}
+    assert _mm(lib, K=100) == E["ERR_ALIGN"]                 # K % 16
+    assert _mm(lib, lda=520) == E["ERR_ALIGN"]
+    assert _mm(lib, N=250, ldc=256) == E["ERR_ALIGN"]         # N % 8
+    assert _mm(lib, lda=256) == E["ERR_SHAPE"]                # lda < K
+    assert _mm(lib, M=-1) == E["ERR_SHAPE"]
+    assert _mm(lib, ka=2) == E["ERR_UNSUPPORTED"]             # COL is not an A kind
+    assert _mm(lib, ka=3, kb=2) == E["ERR_UNSUPPORTED"]       # group A needs block B
+    assert _mm(lib, ka=1, kb=5) == E["ERR_UNSUPPORTED"]
+    assert _mm(lib, A=0) == E["ERR_NULL"]
+    assert _mm(lib, C=0) == E["ERR_NULL"]
+    assert _mm(lib, A=8) == E["ERR_ALIGN"]                    # 16-byte rule
+    assert _mm(lib, K=1 << 17, lda=1 << 17, ldb=1 << 17) == E["ERR_RANGE"]
+    assert _mm(lib, M=0) == E["OK"]                           # empty: nothing launched
+    assert _mm(lib, N=0, ldc=8) == E["OK"]
+
+
+def test_quant_group_rejects_bad_arguments():
+    from column_scaled_gemm_amd import fp8sm
+    lib = fp8sm.lib()
+    E = {v: k for k, v in fp8sm.STATUS.items()}
+    P = ctypes.c_void_p
+
+    def q(**kw):
+        a = dict(x=16, dt=0, M=4, K=256, ldx=256, group=128, flags=0, fmt=0, lay=0, q=16, ldq=256,
+                 s=16)
+        a.update(kw)
+        return lib.fp8sm_quant_group(P(a["x"]), a["dt"], a["M"], a["K"], a["ldx"], a["group"],
+                                     a["flags"], a["fmt"], a["lay"], P(a["q"]), a["ldq"],
+                                     P(a["s"]), P(0))
+    assert q(group=64) == E["ERR_SHAPE"]
+    assert q(K=200, ldx=200, ldq=200) == E["ERR_SHAPE"]       # 200 % 128
+    assert q(K=196, ldx=196, ldq=196, group=196) == E["ERR_ALIGN"]
+    assert q(flags=1) == E["ERR_SHAPE"]                       # fused needs ld_x >= 2K
+    assert q(dt=2) == E["ERR_UNSUPPORTED"]
+    assert q(fmt=3) == E["ERR_UNSUPPORTED"]
+    assert q(lay=2) == E["ERR_UNSUPPORTED"]
+    assert q(flags=4) == E["ERR_UNSUPPORTED"]
+    assert q(x=0) == E["ERR_NULL"]
+    assert q(x=8) == E["ERR_ALIGN"]
+    assert q(M=0) == E["OK"]
+
+
+def test_variant_table_routes_decode_shapes_by_m():
+    from column_scaled_gemm_amd import fp8sm
+    assert fp8sm.variant_count() >= 3
+    names = [fp8sm.variant_name(i) for i in range(fp8sm.variant_count())]
+    assert len(set(names)) == len(names)
+    # the pages' routing regression: an M = 1 down projection must take a
+    # decode variant, not the large-tile path
+    assert fp8sm.variant_name(fp8sm.pick_variant(1, 4096, 14336)).startswith("decode")
+    assert fp8sm.variant_name(fp8sm.pick_variant(16, 14336, 4096)).startswith("decode")
+    assert not fp8sm.variant_name(fp8sm.pick_variant(8320, 21504, 5376)).startswith("decode")
+    prev = fp8sm.force_variant(0)
+    try:
+        assert fp8sm.pick_variant(1, 4096, 4096) == 0
+    finally:
+        fp8sm.force_variant(prev)
+    assert fp8sm.pick_variant(8320, 21504, 5376) == fp8sm.pick_variant(8320, 21504, 5376)

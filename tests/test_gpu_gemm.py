@@ -1,0 +1,247 @@
+"""GPU parity of the scaled GEMMs against the oracle: bit-exact where the
+result is exactly representable, the benchmark spec's bound elsewhere, and bitwise
+row invariance across M and across kernel variants."""
+import numpy as np
+import pytest
+import torch
+
+from column_scaled_gemm_amd import fp8sm, inputs
+from oracle import e4m3, gemm as og, quant as oq
+from gpu_util import (assert_within_tolerance, bf16_bits, cuda, to_gpu_f32, to_gpu_u8)
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+T, ROW, COL = fp8sm.KIND_TENSOR, fp8sm.KIND_ROW, fp8sm.KIND_COL
+
+
+def _mm(a, b, sa, sb, ka=ROW, kb=COL):
+    c = fp8sm.scaled_mm(to_gpu_u8(a), to_gpu_u8(b), to_gpu_f32(sa), to_gpu_f32(sb), ka, kb)
+    torch.cuda.synchronize()
+    return bf16_bits(c)
+
+
+def _variants_for(M):
+    names = []
+    for v in range(fp8sm.variant_count()):
+        n = fp8sm.variant_name(v)
+        cap = {"decode16": 16, "decode32": 32, "decode64": 64}.get(n, 1 << 30)
+        if M <= cap:
+            names.append(v)
+    return names
+
+
+def _mm_variant(v, *args, **kw):
+    prev = fp8sm.force_variant(v)
+    try:
+        return _mm(*args, **kw)
+    finally:
+        fp8sm.force_variant(prev)
+
+
+def test_one_hot_products_of_all_finite_codes_are_exact():
+    c = e4m3.finite_codes()
+    n = 256
+    for kpos, K in [(5, 16), (37, 384), (127, 384), (128, 384), (300, 384)]:
+        A = np.zeros((254, K), np.uint8)
+        B = np.zeros((n, K), np.uint8)
+        A[:, kpos] = c
+        B[:254, kpos] = c
+        for v in _variants_for(254):
+            got = _mm_variant(v, A, B, F32(1), F32(1), T, T)
+            want = og.scaled_mm(A, B, 1.0, 1.0).bits
+            assert np.array_equal(got, want), (kpos, fp8sm.variant_name(v))
+
+
+def test_small_integer_sums_are_exact():
+    # codes of the integers -16..16: every partial sum is an integer below
+    # 2^24, so fp32 accumulation is exact and the bf16 rounding is the oracle's
+    vals = np.arange(-16, 17, dtype=F32)
+    codes = e4m3.encode(vals)
+    r = inputs.rng(11)
+    A = codes[r.integers(0, 33, (70, 1024))]
+    B = codes[r.integers(0, 33, (136, 1024))]
+    want = og.scaled_mm(A, B, 1.0, 1.0).bits
+    for v in _variants_for(70):
+        assert np.array_equal(_mm_variant(v, A, B, np.ones(70, F32), np.ones(136, F32)), want), v
+
+
+def test_zero_rows_give_positive_zero():
+    A = inputs.random_codes((40, 512), seed=12)
+    B = inputs.random_codes((64, 512), seed=13)
+    A[3] = 0
+    A[17] = 0x80
+    got = _mm(A, B, np.ones(40, F32), np.ones(64, F32))
+    assert np.all(got[3] == 0) and np.all(got[17] == 0)
+
+
+def _quantized_case(M, N, K, seed, outliers=True):
+    w = inputs.rowwise(M, N, K, seed=seed, outliers=outliers)
+    qa = oq.quant_group(inputs.widen(w.x), K)
+    qb = oq.quant_group(inputs.widen(w.w), K)
+    return qa.codes, qb.codes, qa.scale.reshape(-1), qb.scale.reshape(-1)
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 16), (37, 264, 80), (100, 136, 208), (130, 520, 1040),
+                                   (64, 256, 512), (257, 128, 4096), (33, 1000, 2064)])
+def test_ragged_shapes_every_variant_bitwise_equal_and_within_bound(shape):
+    M, N, K = shape
+    print(f"[case] ragged M={M} N={N} K={K}", flush=True)
+    A, B, sa, sb = _quantized_case(M, N, K, seed=M + N + K)
+    res = og.scaled_mm(A, B, sa, sb)
+    outs = {}
+    for v in _variants_for(M):
+        outs[v] = _mm_variant(v, A, B, sa, sb)
+        assert_within_tolerance(outs[v], res, K, f"{shape} {fp8sm.variant_name(v)}")
+    first = next(iter(outs.values()))
+    for v, o in outs.items():
+        assert np.array_equal(o, first), f"variant {fp8sm.variant_name(v)} differs bitwise"
+
+
+def test_rows_do_not_depend_on_m():
+    # sglang PR #44861 reviewers' check: rows of an M-row call against the same
+    # rows inside a 101-row call, K = 6144, N = 5120
+    M0, N, K = 101, 5120, 6144
+    A, B, sa, sb = _quantized_case(M0, N, K, seed=21, outliers=False)
+    full = _mm(A, B, sa, sb)
+    for M in (1, 8, 16, 37, 64, 100):
+        part = _mm(A[:M], B, sa[:M], sb)
+        assert np.array_equal(part, full[:M]), M
+    res = og.scaled_mm(A, B, sa, sb)
+    assert_within_tolerance(full, res, K, "row-invariance case")
+
+
+def test_power_of_two_scale_linearity_is_bitwise():
+    A, B, sa, sb = _quantized_case(48, 256, 1024, seed=22)
+    base = _mm(A, B, sa, sb)
+    twice = _mm(A, B, (sa * F32(4)).astype(F32), (sb * F32(0.5)).astype(F32))
+    b = base.astype(np.uint32) << 16
+    t = twice.astype(np.uint32) << 16
+    assert np.array_equal((b.view(F32) * F32(2)).view(np.uint32), t)
+
+
+def test_per_tensor_equals_rowwise_with_broadcast_scales():
+    A = inputs.random_codes((24, 768), seed=23)
+    B = inputs.random_codes((96, 768), seed=24)
+    s1, s2 = F32(0.0123), F32(0.000456)
+    x = _mm(A, B, s1, s2, T, T)
+    y = _mm(A, B, np.full(24, s1), np.full(96, s2), ROW, COL)
+    assert np.array_equal(x, y)
+    assert_within_tolerance(x, og.scaled_mm(A, B, s1, s2), 768, "per-tensor random codes")
+
+
+def test_tiny_workload_pipeline():
+    # quant of both operands on the GPU, compared bit-exactly, then the GEMM
+    w = inputs.workload("tiny")
+    M, N, K = inputs.ROWWISE_SHAPES["tiny"]
+    qa, sa = fp8sm.quant_group(w.x.to(cuda()), -1)
+    qb, sb = fp8sm.quant_group(w.w.to(cuda()), -1)
+    c = fp8sm.scaled_mm(qa, qb, sa.reshape(-1), sb.reshape(-1), ROW, COL)
+    torch.cuda.synchronize()
+    oa = oq.quant_group(inputs.widen(w.x), K)
+    ob = oq.quant_group(inputs.widen(w.w), K)
+    assert np.array_equal(qa.cpu().numpy(), oa.codes)
+    assert np.array_equal(qb.cpu().numpy(), ob.codes)
+    res = og.scaled_mm(oa.codes, ob.codes, oa.scale.reshape(-1), ob.scale.reshape(-1))
+    assert_within_tolerance(bf16_bits(c), res, K, "tiny 64x256x512")
+
+
+@pytest.mark.parametrize("N", list(inputs.DECODE_NS))
+def test_decode_workload_per_tensor(N):
+    d = inputs.decode()
+    xs = torch.tensor([d.x_scale], dtype=torch.float32, device=cuda())
+    ws = torch.tensor([d.w_scale[N]], dtype=torch.float32, device=cuda())
+    qx = fp8sm.quant_static(d.x.to(cuda()), xs)
+    qw = fp8sm.quant_static(d.w[N].to(cuda()), ws)
+    ox = oq.quant_static(inputs.widen(d.x), F32(d.x_scale))
+    ow = oq.quant_static(inputs.widen(d.w[N]), F32(d.w_scale[N]))
+    torch.cuda.synchronize()
+    assert np.array_equal(qx.cpu().numpy(), ox)
+    assert np.array_equal(qw.cpu().numpy(), ow)
+    res = og.scaled_mm(ox, ow, F32(d.x_scale), F32(d.w_scale[N]))
+    outs = {}
+    for M in inputs.DECODE_MS:
+        c = fp8sm.scaled_mm(qx[:M], qw, xs, ws, T, T)
+        torch.cuda.synchronize()
+        outs[M] = bf16_bits(c)
+    assert_within_tolerance(outs[16], res, inputs.DECODE_K, f"decode N={N}")
+    for M in inputs.DECODE_MS:
+        assert np.array_equal(outs[M], outs[16][:M]), M
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_fused_blockwise_workload(dtype):
+    f = inputs.fused()
+    x = f.gu_bf16 if dtype == torch.bfloat16 else f.gu_fp16
+    qa, ea = fp8sm.quant_group(x.to(cuda()), 128, fp8sm.SCALE_UE8M0_BYTE, fuse_silu_mul=True)
+    qb, sb = fp8sm.quant_weight_block128(f.w.to(cuda()))
+    c = fp8sm.scaled_mm(qa, qb, ea, sb, fp8sm.KIND_GROUP128_UE8M0, fp8sm.KIND_BLOCK128)
+    torch.cuda.synchronize()
+    oa = oq.quant_group_silu_mul(inputs.widen(x), 128, pow2=True)
+    ob_codes, ob_scale = oq.quant_weight_block(inputs.widen(f.w))
+    assert np.array_equal(qa.cpu().numpy(), oa.codes)
+    assert np.array_equal(ea.cpu().numpy(), oa.ue8m0_byte)
+    assert np.array_equal(qb.cpu().numpy(), ob_codes)
+    res = og.blockwise_mm(oa.codes, oa.scale, ob_codes, ob_scale)
+    got = bf16_bits(c)
+    assert np.all(got[f.zero_rows] == 0)
+    assert_within_tolerance(got, res, inputs.FUSED_K, f"fused blockwise {dtype}")
+
+
+def test_blockwise_fp32_group_scales_ragged():
+    r = inputs.rng(25)
+    M, N, K = 70, 264, 400
+    A = inputs.random_codes((M, K), seed=26)
+    B = inputs.random_codes((N, K), seed=27)
+    sa = np.exp2(r.uniform(-12, -4, (M, 4))).astype(F32)
+    sb = np.exp2(r.uniform(-12, -4, (3, 4))).astype(F32)
+    c = fp8sm.scaled_mm(to_gpu_u8(A), to_gpu_u8(B), to_gpu_f32(sa), to_gpu_f32(sb),
+                        fp8sm.KIND_GROUP128_FP32, fp8sm.KIND_BLOCK128)
+    torch.cuda.synchronize()
+    assert_within_tolerance(bf16_bits(c), og.blockwise_mm(A, sa, B, sb), K, "blockwise fp32 ragged")
+
+
+def test_k_zero_writes_zeros():
+    c = torch.full((5, 16), 7.0, dtype=torch.bfloat16, device=cuda())
+    a = torch.zeros((5, 16), dtype=torch.uint8, device=cuda())
+    b = torch.zeros((16, 16), dtype=torch.uint8, device=cuda())
+    s = torch.ones(16, dtype=torch.float32, device=cuda())
+    st = fp8sm.lib().fp8sm_scaled_mm(a.data_ptr(), 16, b.data_ptr(), 16, c.data_ptr(), 16, 5, 16, 0,
+                                     ROW, s.data_ptr(), COL, s.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert st == 0 and torch.all(c == 0)
+
+
+def _sampled_full_size(name):
+    M, N, K = inputs.ROWWISE_SHAPES[name]
+    w = inputs.workload(name)
+    qa, sa = fp8sm.quant_group(w.x.to(cuda()), -1)
+    qb, sb = fp8sm.quant_group(w.w.to(cuda()), -1)
+    c = fp8sm.scaled_mm(qa, qb, sa.reshape(-1), sb.reshape(-1), ROW, COL)
+    torch.cuda.synchronize()
+    r = inputs.rng(99)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), r.integers(0, M, 24)]))
+    cols = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N), r.integers(0, N, 24)]))
+    # the oracle quantizes only the sampled rows / channels (rows are independent)
+    oa = oq.quant_group(inputs.widen(w.x[torch.from_numpy(rows)]), K)
+    ga = qa[torch.from_numpy(rows).to(cuda())].cpu().numpy()
+    assert np.array_equal(ga, oa.codes)
+    ob_all = oq.quant_group(inputs.widen(w.w), K)
+    assert np.array_equal(qb.cpu().numpy(), ob_all.codes)
+    oa_cols = oq.quant_group(inputs.widen(w.x), K)
+    gpu_bits = bf16_bits(c)
+    res_r = og.scaled_mm(oa.codes, ob_all.codes, oa.scale.reshape(-1), ob_all.scale.reshape(-1))
+    assert_within_tolerance(gpu_bits[rows], res_r, K, f"{name} sampled rows")
+    res_c = og.scaled_mm(oa_cols.codes, ob_all.codes[cols], oa_cols.scale.reshape(-1),
+                         ob_all.scale.reshape(-1)[cols])
+    assert_within_tolerance(gpu_bits[:, cols], res_c, K, f"{name} sampled cols")
+
+
+@pytest.mark.parametrize("name", ["qkv", "mlp_down"])
+def test_full_size_rowwise_sampled(name):
+    _sampled_full_size(name)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["mlp_gateup_23216", "mlp_gateup_15760"])
+def test_full_size_rowwise_sampled_large(name):
+    _sampled_full_size(name)
