@@ -1,0 +1,155 @@
+"""Benchmark of the FP8 quant + scaled-GEMM hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input:
+per-token E4M3FN quant of the bf16 activations (fp32 scales), then the rowwise
+scaled GEMM against pre-quantized per-channel weights, writing bf16.  The
+default workload is the attention-QKV projection the pages benchmark
+("Route large SM90 row/column-scaled FP8 GEMMs to Torch", Kernel results):
+M=8320, K=5376, N=21504.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (rank 0).  `value` is GEMM TFLOP/s over the whole step
+(2*M*N*K / step time, quant included).  `roofline` is the GEMM kernel's own
+achieved rate (HIP events around each GEMM launch on the launch stream)
+against the peak of the matrix instruction it runs on (bf16 dense MFMA,
+2.5 PFLOP/s), with `fp8_peak_frac` against the 5.0 PFLOP/s dense FP8 peak
+for reference.  `cpu_baseline` times the CPU oracle on a bounded sample of the
+same workload (a block of rows: their per-token quant plus their GEMM rows).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp8_scaled_mm TFLOP/s and % of FP8 MFMA peak on H3 dense shapes; quant GB/s"
+PEAK_BF16_MFMA = 2500.0     # TFLOP/s, dense
+PEAK_FP8_MFMA = 5000.0      # TFLOP/s, dense
+PEAK_HBM = 8000.0           # GB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="qkv",
+                   choices=["qkv", "mlp_gateup_23216", "mlp_gateup_15760", "mlp_down", "tiny"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def cpu_baseline(w, M, N, K, target_s):
+    """Time the CPU oracle on the first R rows of the workload (quant of those
+    rows + their GEMM rows against the full weight), R sized to ~target_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from column_scaled_gemm_amd import inputs
+    from oracle import gemm as og, quant as oq
+
+    ob = oq.quant_group(inputs.widen(w.w), K)            # offline weight quant, untimed
+
+    def run(R):
+        t0 = time.perf_counter()
+        oa = oq.quant_group(inputs.widen(w.x[:R]), K)
+        og.scaled_mm(oa.codes, ob.codes, oa.scale.reshape(-1), ob.scale.reshape(-1))
+        return time.perf_counter() - t0
+
+    R = 16
+    t = run(R)
+    R = int(max(16, min(M, R * target_s / max(t, 1e-3))))
+    t = run(R)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(2.0 * R * N * K / t / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"first {R} of {M} rows: per-token quant + GEMM rows vs the full "
+                      f"{N}x{K} weight ({t:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU path is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from column_scaled_gemm_amd import fp8sm, inputs
+
+    dev = torch.device("cuda:0")
+    M, N, K = inputs.ROWWISE_SHAPES[args.workload]
+    w = inputs.workload(args.workload)
+    x = w.x.to(dev)
+    qb, sb = fp8sm.quant_group(w.w.to(dev), -1)            # weights: quantized once
+    sb = sb.reshape(-1)
+    qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, 1), dtype=torch.float32, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        fp8sm.quant_group(x, -1, q=qa, scales=sa, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        fp8sm.scaled_mm(qa, qb, sa.reshape(-1), sb, fp8sm.KIND_ROW, fp8sm.KIND_COL, c=c,
+                        stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flop = 2.0 * M * N * K
+    value = flop / (ms_step * 1e-3) / 1e12
+    gemm_tflops = flop / (gemm_ms * 1e-3) / 1e12
+    quant_ms = max(ms_step - gemm_ms, 1e-9)
+    quant_bytes = 2 * M * K + M * K + 4 * M
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: per-token quant bf16[{M},{K}] + rowwise "
+                               f"fp8_scaled_mm {M}x{K}x{N} -> bf16",
+                   "M": M, "N": N, "K": K, "kernel_variant": fp8sm.variant_name(
+                       fp8sm.pick_variant(M, N, K))},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 3),
+                     "peak": PEAK_BF16_MFMA, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_BF16_MFMA, 4), "traffic": None},
+        "fp8_peak_frac": round(gemm_tflops / PEAK_FP8_MFMA, 4),
+        "gemm_us": round(gemm_ms * 1e3, 2),
+        "quant_us_est": round(quant_ms * 1e3, 2),
+        "quant_GBps_est": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, M, N, K, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

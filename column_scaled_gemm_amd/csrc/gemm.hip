@@ -30,7 +30,10 @@
 
 namespace fp8sm {
 
-constexpr int kPromoteTiles = 4;  // 512-wide K blocks per fp32 partial
+#ifndef FP8SM_PROMOTE_TILES
+#define FP8SM_PROMOTE_TILES 4
+#endif
+constexpr int kPromoteTiles = FP8SM_PROMOTE_TILES;  // 128-wide K tiles per fp32 partial
 
 enum { MODE_ROWWISE = 0, MODE_BLOCK_UE8M0 = 1, MODE_BLOCK_FP32 = 2 };
 
