@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="qkv",
                    choices=["qkv", "mlp_gateup_23216", "mlp_gateup_15760", "mlp_down", "tiny"])
+    p.add_argument("--variant", default=None,
+                   help="force a GEMM kernel variant by name (default: the dispatch table)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -81,6 +83,9 @@ def main():
     from column_scaled_gemm_amd import fp8sm, inputs
 
     dev = torch.device("cuda:0")
+    if args.variant:
+        names = [fp8sm.variant_name(i) for i in range(fp8sm.variant_count())]
+        fp8sm.force_variant(names.index(args.variant))
     M, N, K = inputs.ROWWISE_SHAPES[args.workload]
     w = inputs.workload(args.workload)
     x = w.x.to(dev)

@@ -5,42 +5,31 @@
 // form): C[m,n] = bf16(acc[m,n] * sa[m] * sb[n]), acc = sum_k A[m,k] * B[n,k],
 // A [M][lda] and B [N][ldb] E4M3FN with K contiguous.
 //
-// Arithmetic, identical in every variant (so a row of C never depends on M,
-// on its neighbours, or on the variant the shape dispatch picked -- the
-// property sglang PR #44861's reviewers checked row by row):
+// Arithmetic of the rowwise / per-tensor path, identical in every variant so a
+// row of C never depends on M, on its neighbours or on the variant the shape
+// dispatch picked (the property sglang PR #44861's reviewers checked row by
+// row):
 //  * fp8 codes are widened exactly to bf16 in registers and multiplied on the
 //    bf16 matrix cores (v_mfma_f32_16x16x32_bf16).  The fp8 matrix
 //    instructions were measured to sum each run of 8 products with the
-//    smaller ones truncated ~13 bits below the largest, far outside fp32
+//    smaller ones truncated ~13 bits below the largest -- far outside fp32
 //    accumulation; the bf16 instruction keeps near-fp32 precision.
-//  * Within a 128-wide K tile, MFMA step s (0..3) of lane group g (0..3)
-//    multiplies k = 32g + 8s + j, j = 0..7.
-//  * Products of kPromoteTiles consecutive K tiles are chained into a fresh
-//    fp32 partial (the first MFMA of a block starts from zero); partials are
-//    added into an fp32 master in ascending block order.
-//  * Epilogue: bf16_rne((master * sa[m]) * sb[n]).
-// The decode kernel splits the K blocks across wavefronts but merges the
-// partials in the same ascending order, so it is bitwise identical.
+//  * K is walked in 64-wide chunks, ascending.  Within a chunk, MFMA step s
+//    (0, 1) of lane group g (0..3) multiplies k = 16g + 8s + j, j = 0..7.
+//    Positions past K hold zero codes.
+//  * One fp32 accumulator per output is chained through every step, starting
+//    from zero (fp32 accumulation, as the path is specified).
+//  * Epilogue: bf16_rne((acc * sa[m]) * sb[n]).
 //
 // Blockwise (1x128 activation groups x 128x128 weight blocks): a fresh fp32
-// partial per 128-wide K tile, multiplied by sa[m,kb] * sb[n/128,kb] in fp64
+// partial per 128-wide K block, multiplied by sa[m,kb] * sb[n/128,kb] in fp64
 // and accumulated in an fp64 master; bf16 of the master at the end.
 #include "device_common.h"
 #include "launch.h"
 
 namespace fp8sm {
 
-#ifndef FP8SM_PROMOTE_TILES
-#define FP8SM_PROMOTE_TILES 4
-#endif
-constexpr int kPromoteTiles = FP8SM_PROMOTE_TILES;  // 128-wide K tiles per fp32 partial
-
-enum { MODE_ROWWISE = 0, MODE_BLOCK_UE8M0 = 1, MODE_BLOCK_FP32 = 2 };
-
-// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row, chosen so
-// that the 16 rows read by one 16-lane group (and the 8 rows of any 8-lane
-// phase) land in distinct bank groups.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row << 2)) & 7; }
+constexpr int kChunk = 64;  // K bytes per pipeline stage / canonical chunk
 
 __device__ __forceinline__ bf16x8 widen_e4m3_x8(uint32_t d0, uint32_t d1) {
   const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
@@ -50,18 +39,20 @@ __device__ __forceinline__ bf16x8 widen_e4m3_x8(uint32_t d0, uint32_t d1) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// One 128-wide K tile for TM x TN 16x16 output tiles.  af/bf hold each lane's
-// 32 bytes (k = 32g .. 32g+31 of the tile) for every row/column subtile.
+// One canonical 64-wide chunk for TM x TN 16x16 output tiles: fa/fb hold each
+// lane's 16 bytes (k = 16g .. 16g+15 of the chunk) per row / column subtile.
 template <int TM, int TN>
-__device__ __forceinline__ void mma_tile128(const uint32_t (&af)[TM][8], const uint32_t (&bf)[TN][8],
+__device__ __forceinline__ void mma_chunk64(const uint4 (&fa)[TM], const uint4 (&fb)[TN],
                                             f32x4 (&acc)[TM][TN]) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < 2; ++s) {
     bf16x8 a[TM], b[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = widen_e4m3_x8(af[i][2 * s], af[i][2 * s + 1]);
+    for (int i = 0; i < TM; ++i)
+      a[i] = s == 0 ? widen_e4m3_x8(fa[i].x, fa[i].y) : widen_e4m3_x8(fa[i].z, fa[i].w);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = widen_e4m3_x8(bf[j][2 * s], bf[j][2 * s + 1]);
+    for (int j = 0; j < TN; ++j)
+      b[j] = s == 0 ? widen_e4m3_x8(fb[j].x, fb[j].y) : widen_e4m3_x8(fb[j].z, fb[j].w);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -98,64 +89,239 @@ __device__ __forceinline__ void tile_coords(int bid, int nbid, int tiles_m, int 
   tn = r / gm;
 }
 
+// 16 zero bytes: the DMA source for chunk positions past K.
+__device__ __attribute__((aligned(16))) uint8_t g_zero16[16];
+
+// 16-byte global -> LDS copy (global_load_lds_dwordx4).  Issued as inline asm
+// so the compiler does not wait for every such copy before each LDS read; the
+// kernel waits for exactly the stages it needs with wait_vmcnt.  lds_addr is
+// the wave-uniform LDS byte address of lane 0's destination; lane i writes
+// lds_addr + 16 i.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_addr), "v"(g)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS chunk swizzle for 64-byte rows: the 16-byte chunk c of row r is stored
+// at position c ^ swz16(r mod 16).  A 16-lane group reading the same chunk of
+// 16 consecutive rows (and any 8-lane phase of it) then hits distinct banks.
+__device__ __forceinline__ int swz16(int x) { return ((x >> 1) ^ (x >> 3)) & 3; }
+
 // ---------------------------------------------------------------------------
-// LDS-staged tile kernel: BM x BN workgroup tile, 4 wavefronts in a WM x WN
-// grid, 128-wide K tiles double-buffered through LDS (16-byte global loads
-// into registers, swizzled 16-byte LDS stores, one barrier per K tile).
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(
+// Rowwise tile kernel: BM x BN workgroup tile, 4 wavefronts in a 2 x 2 grid
+// (wave tile BM/2 x BN/2), 64-wide K chunks in a 4-slot LDS ring filled by
+// global->LDS DMA three chunks ahead, one barrier per chunk.
+template <int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_rowwise_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
-    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const void* __restrict__ sa_p,
-    int sa_vec, const float* __restrict__ sb_p, int sb_vec, int tiles_m, int tiles_n) {
-  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
+    int sa_vec, const float* __restrict__ sb, int sb_vec, int tiles_m, int tiles_n) {
+  constexpr int TM = BM / 32, TN = BN / 32;
   constexpr int ROWS = BM + BN;
-  static_assert((ROWS * 8) % 256 == 0, "tile rows must split evenly over 256 threads");
-  constexpr int CPT = ROWS * 8 / 256;
-  constexpr int STAGE = ROWS * 128;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  constexpr int SLOT = ROWS * kChunk;          // bytes per ring slot
+  constexpr int SEGS = SLOT / 1024;            // 1 KB segments per slot (16 rows each)
+  constexpr int DPS = SEGS / 4;                // DMA instructions per thread per stage
+  constexpr int NSLOT = 4;
+  static_assert(SEGS % 4 == 0, "segments must split over the four wavefronts");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSLOT * SLOT];
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w / WN, wn = w % WN;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w >> 1, wn = w & 1;
   const int g = lane >> 4, r16 = lane & 15;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
 
+  // DMA sources: instruction i of wave w fills segment i*4+w of a slot; lane
+  // l writes row (segment*16 + l/4), position l%4, which holds chunk
+  // (l%4) ^ swz16(l/4).
+  const uint8_t* src[DPS];
+  int koff[DPS];
+#pragma unroll
+  for (int i = 0; i < DPS; ++i) {
+    const int seg = i * 4 + w;
+    const int row = seg * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz16(lane >> 2);
+    koff[i] = c * 16;
+    src[i] = row < BM ? A + (int64_t)min(m0 + row, M - 1) * lda + koff[i]
+                      : B + (int64_t)min(n0 + row - BM, N - 1) * ldb + koff[i];
+  }
+  const int nkc = (K + kChunk - 1) / kChunk;
+  auto issue = [&](int kc) {
+    const uint32_t slot = lds0 + (uint32_t)((kc & (NSLOT - 1)) * SLOT);
+    const int64_t kb = (int64_t)kc * kChunk;
+#pragma unroll
+    for (int i = 0; i < DPS; ++i) {
+      const void* p = kb + koff[i] < K ? (const void*)(src[i] + kb) : (const void*)g_zero16;
+      dma16(p, slot + (uint32_t)((i * 4 + w) * 1024));
+    }
+  };
+
+  // fragment read offsets (bytes within a slot)
+  const int a_off = (wm * (BM / 2) + r16) * kChunk + ((g ^ swz16(r16)) << 4);
+  const int b_off = (BM + wn * (BN / 2) + r16) * kChunk + ((g ^ swz16(r16)) << 4);
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0);
+  if (nkc > 1) issue(1);
+  if (nkc > 2) issue(2);
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int after = min(2, nkc - 1 - kc);  // stages issued after kc, still in flight
+    if (after == 2)
+      wait_vmcnt<2 * DPS>();
+    else if (after == 1)
+      wait_vmcnt<DPS>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // chunk kc visible to all; slot of chunk kc-1 free
+    if (kc + 3 < nkc) issue(kc + 3);
+    const uint8_t* slot = lds + (kc & (NSLOT - 1)) * SLOT;
+    uint4 fa[TM], fb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const uint4*>(slot + a_off + i * 16 * kChunk);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const uint4*>(slot + b_off + j * 16 * kChunk);
+    mma_chunk64<TM, TN>(fa, fb, acc);
+  }
+
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int c = n0 + wn * (BN / 2) + 16 * j + r16;
+    const float sbc = sb[sb_vec ? min(c, N - 1) : 0];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = m0 + wm * (BM / 2) + 16 * i + 4 * g + v;
+        if (r < M && c < N)
+          C[(int64_t)r * ldc + c] = f32_to_bf16_rne(rowwise_epilogue(acc[i][j][v], sa[sa_vec ? r : 0], sbc));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel (M <= 16 * TM): one wavefront owns 16 output columns and walks
+// all of K in the canonical order, streaming A and B straight into registers
+// D chunks ahead (software pipelined: chunk c + D is requested while chunk c
+// is multiplied).
+template <int TM, int D>
+__global__ __launch_bounds__(64) void gemm_decode_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
+    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
+    int sa_vec, const float* __restrict__ sb, int sb_vec) {
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int n0 = blockIdx.x * 16;
+  const int nkc = (K + kChunk - 1) / kChunk;
+  const uint8_t* brow = B + (int64_t)min(n0 + r16, N - 1) * ldb + 16 * g;
+  const uint8_t* arow[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) arow[i] = A + (int64_t)min(16 * i + r16, M - 1) * lda + 16 * g;
+  const int kl = 16 * g;
+  auto ld = [&](const uint8_t* p, int kc) -> uint4 {
+    const int64_t k0 = (int64_t)kc * kChunk;
+    return k0 + kl < K ? *reinterpret_cast<const uint4*>(p + k0) : make_uint4(0, 0, 0, 0);
+  };
+  f32x4 acc[TM][1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 rb[D], ra[D][TM];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    rb[d] = ld(brow, d);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ra[d][i] = ld(arow[i], d);
+  }
+  for (int kc0 = 0; kc0 < nkc; kc0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (kc0 + d < nkc) {
+        uint4 fb[1] = {rb[d]};
+        uint4 fa[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = ra[d][i];
+        mma_chunk64<TM, 1>(fa, fb, acc);
+      }
+      rb[d] = ld(brow, kc0 + d + D);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ra[d][i] = ld(arow[i], kc0 + d + D);
+    }
+  }
+  const int c = n0 + r16;
+  if (c >= N) return;
+  const float sbc = sb[sb_vec ? c : 0];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * i + 4 * g + v;
+      if (r < M)
+        C[(int64_t)r * ldc + c] = f32_to_bf16_rne(rowwise_epilogue(acc[i][0][v], sa[sa_vec ? r : 0], sbc));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Blockwise kernel: 128 x 128 workgroup tile, 4 wavefronts of 64 x 64, 128-wide
+// K tiles double-buffered through LDS (register-staged 16-byte loads, XOR
+// swizzled 128-byte rows).  Each K tile is one scale block.
+__device__ __forceinline__ int swz8(int row) { return ((row >> 1) ^ (row << 2)) & 7; }
+
+template <bool UE8M0>
+__global__ __launch_bounds__(256, 1) void gemm_blockwise_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
+    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const void* __restrict__ sa_p,
+    const float* __restrict__ sb_p, int tiles_m, int tiles_n) {
+  constexpr int BM = 128, BN = 128, TM = 4, TN = 4;
+  constexpr int ROWS = BM + BN, CPT = ROWS * 8 / 256, STAGE = ROWS * 128;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int g = lane >> 4, r16 = lane & 15;
   const uint8_t* gsrc[CPT];
   int ldst[CPT], kc[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int id = t + 256 * i, row = id >> 3, c = id & 7;
-    if (row < BM)
-      gsrc[i] = A + (int64_t)min(m0 + row, M - 1) * lda + c * 16;
-    else
-      gsrc[i] = B + (int64_t)min(n0 + row - BM, N - 1) * ldb + c * 16;
-    ldst[i] = row * 128 + ((c ^ swz(row)) << 4);
+    gsrc[i] = row < BM ? A + (int64_t)min(m0 + row, M - 1) * lda + c * 16
+                       : B + (int64_t)min(n0 + row - BM, N - 1) * ldb + c * 16;
+    ldst[i] = row * 128 + ((c ^ swz8(row)) << 4);
     kc[i] = c * 16;
   }
   const int nk = (K + 127) / 128;
-  const int KB = nk;
   uint4 pre[CPT];
-
-  f32x4 part[TM][TN], mast[TM][TN];
-  double mastd[TM][TN][4];
+  f32x4 part[TM][TN];
+  double mast[TM][TN][4];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mast[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) mastd[i][j][v] = 0.0;
+      for (int v = 0; v < 4; ++v) mast[i][j][v] = 0.0;
     }
-
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
     pre[i] = kc[i] < K ? *reinterpret_cast<const uint4*>(gsrc[i]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) *reinterpret_cast<uint4*>(lds + ldst[i]) = pre[i];
   __syncthreads();
-
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) {
       const int64_t koff = (int64_t)(kt + 1) * 128;
@@ -165,62 +331,44 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(
                                   : make_uint4(0, 0, 0, 0);
     }
     const uint8_t* base = lds + (kt & 1) * STAGE;
-    uint32_t af[TM][8], bfr[TN][8];
+    // each 128-wide tile is two 64-wide halves; lane group g takes 16 bytes of
+    // each half per row (k = 64h + 16g + 8s + j within the tile)
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * (BM / WM) + 16 * i + r16;
-      const uint8_t* p = base + row * 128;
-      const uint4 lo = *reinterpret_cast<const uint4*>(p + (((2 * g) ^ swz(row)) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(p + (((2 * g + 1) ^ swz(row)) << 4));
-      af[i][0] = lo.x; af[i][1] = lo.y; af[i][2] = lo.z; af[i][3] = lo.w;
-      af[i][4] = hi.x; af[i][5] = hi.y; af[i][6] = hi.z; af[i][7] = hi.w;
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = BM + wn * (BN / WN) + 16 * j + r16;
-      const uint8_t* p = base + row * 128;
-      const uint4 lo = *reinterpret_cast<const uint4*>(p + (((2 * g) ^ swz(row)) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(p + (((2 * g + 1) ^ swz(row)) << 4));
-      bfr[j][0] = lo.x; bfr[j][1] = lo.y; bfr[j][2] = lo.z; bfr[j][3] = lo.w;
-      bfr[j][4] = hi.x; bfr[j][5] = hi.y; bfr[j][6] = hi.z; bfr[j][7] = hi.w;
-    }
-    mma_tile128<TM, TN>(af, bfr, part);
-
-    if constexpr (MODE == MODE_ROWWISE) {
-      if ((kt + 1) % kPromoteTiles == 0 || kt + 1 == nk) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            mast[i][j] += part[i][j];
-            part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-      }
-    } else {
-      // blockwise: this K tile is exactly one 128-wide scale block
-      const float sbv = sb_p[(int64_t)(n0 / 128) * KB + kt];
+    for (int h = 0; h < 2; ++h) {
+      uint4 fa[TM], fb[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = min(m0 + wm * (BM / WM) + 16 * i + 4 * g + v, M - 1);
-          double s64;
-          if constexpr (MODE == MODE_BLOCK_UE8M0) {
-            const int byte = static_cast<const uint8_t*>(sa_p)[(int64_t)r * KB + kt];
-            s64 = ldexp((double)sbv, byte - 127);
-          } else {
-            s64 = (double)static_cast<const float*>(sa_p)[(int64_t)r * KB + kt] * (double)sbv;
-          }
-#pragma unroll
-          for (int j = 0; j < TN; ++j) mastd[i][j][v] = fma((double)part[i][j][v], s64, mastd[i][j][v]);
-        }
+        const int row = wm * 64 + 16 * i + r16;
+        fa[i] = *reinterpret_cast<const uint4*>(base + row * 128 + (((4 * h + g) ^ swz8(row)) << 4));
       }
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TN; ++j) {
+        const int row = BM + wn * 64 + 16 * j + r16;
+        fb[j] = *reinterpret_cast<const uint4*>(base + row * 128 + (((4 * h + g) ^ swz8(row)) << 4));
+      }
+      mma_chunk64<TM, TN>(fa, fb, part);
     }
-
+    const float sbv = sb_p[(int64_t)tn * nk + kt];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = min(m0 + wm * 64 + 16 * i + 4 * g + v, M - 1);
+        double s64;
+        if constexpr (UE8M0) {
+          const int byte = static_cast<const uint8_t*>(sa_p)[(int64_t)r * nk + kt];
+          s64 = ldexp((double)sbv, byte - 127);
+        } else {
+          s64 = (double)static_cast<const float*>(sa_p)[(int64_t)r * nk + kt] * (double)sbv;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) mast[i][j][v] = fma((double)part[i][j][v], s64, mast[i][j][v]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (kt + 1 < nk) {
       uint8_t* nb = lds + ((kt + 1) & 1) * STAGE;
 #pragma unroll
@@ -228,117 +376,17 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(
     }
     __syncthreads();
   }
-
-  // epilogue
-  const float* sa_f = static_cast<const float*>(sa_p);
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int c = n0 + wn * (BN / WN) + 16 * j + r16;
-    const float sbc = MODE == MODE_ROWWISE ? sb_p[sb_vec ? min(c, N - 1) : 0] : 1.0f;
+    const int c = n0 + wn * 64 + 16 * j + r16;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int r = m0 + wm * (BM / WM) + 16 * i + 4 * g + v;
-        if (r < M && c < N) {
-          float val;
-          if constexpr (MODE == MODE_ROWWISE)
-            val = rowwise_epilogue(mast[i][j][v], sa_f[sa_vec ? r : 0], sbc);
-          else
-            val = (float)mastd[i][j][v];
-          C[(int64_t)r * ldc + c] = f32_to_bf16_rne(val);
-        }
+        const int r = m0 + wm * 64 + 16 * i + 4 * g + v;
+        if (r < M && c < N) C[(int64_t)r * ldc + c] = f32_to_bf16_rne((float)mast[i][j][v]);
       }
-    }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Decode kernel (M <= 16 * TM): a workgroup owns 16 output columns; its four
-// wavefronts take the 512-wide K blocks in turn (block b by wavefront b % 4),
-// each streaming its operands straight from global memory into registers, and
-// wavefront 0 adds the partials into the master in ascending block order.
-template <int TM>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(
-    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
-    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
-    int sa_vec, const float* __restrict__ sb, int sb_vec) {
-  __shared__ f32x4 red[4][TM][64];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int n0 = blockIdx.x * 16;
-  const int nk = (K + 127) / 128;
-  const int nblk = (nk + kPromoteTiles - 1) / kPromoteTiles;
-  const uint8_t* brow = B + (int64_t)min(n0 + r16, N - 1) * ldb + 32 * g;
-  const uint8_t* arow[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) arow[i] = A + (int64_t)min(16 * i + r16, M - 1) * lda + 32 * g;
-
-  f32x4 mast[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) mast[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int b0 = 0; b0 < nblk; b0 += 4) {
-    const int blk = b0 + w;
-    f32x4 part[TM][1];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) part[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (blk < nblk) {
-      uint4 bv[kPromoteTiles][2], av[kPromoteTiles][TM][2];
-#pragma unroll
-      for (int tt = 0; tt < kPromoteTiles; ++tt) {
-        const int64_t k0 = (int64_t)(blk * kPromoteTiles + tt) * 128 + 32 * g;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bool ok = k0 + 16 * h < K;
-          bv[tt][h] = ok ? *reinterpret_cast<const uint4*>(brow + (k0 - 32 * g) + 16 * h)
-                         : make_uint4(0, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-            av[tt][i][h] = ok ? *reinterpret_cast<const uint4*>(arow[i] + (k0 - 32 * g) + 16 * h)
-                              : make_uint4(0, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int tt = 0; tt < kPromoteTiles; ++tt) {
-        if (blk * kPromoteTiles + tt < nk) {
-          uint32_t af[TM][8], bfr[1][8];
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            af[i][0] = av[tt][i][0].x; af[i][1] = av[tt][i][0].y;
-            af[i][2] = av[tt][i][0].z; af[i][3] = av[tt][i][0].w;
-            af[i][4] = av[tt][i][1].x; af[i][5] = av[tt][i][1].y;
-            af[i][6] = av[tt][i][1].z; af[i][7] = av[tt][i][1].w;
-          }
-          bfr[0][0] = bv[tt][0].x; bfr[0][1] = bv[tt][0].y; bfr[0][2] = bv[tt][0].z;
-          bfr[0][3] = bv[tt][0].w; bfr[0][4] = bv[tt][1].x; bfr[0][5] = bv[tt][1].y;
-          bfr[0][6] = bv[tt][1].z; bfr[0][7] = bv[tt][1].w;
-          mma_tile128<TM, 1>(af, bfr, part);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) red[w][i][lane] = part[i][0];
-    __syncthreads();
-    if (w == 0) {
-      for (int ww = 0; ww < 4; ++ww)
-        if (b0 + ww < nblk)
-#pragma unroll
-          for (int i = 0; i < TM; ++i) mast[i] += red[ww][i][lane];
-    }
-    __syncthreads();
-  }
-  if (w != 0) return;
-  const int c = n0 + r16;
-  if (c >= N) return;
-  const float sbc = sb[sb_vec ? c : 0];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = 16 * i + 4 * g + v;
-      if (r < M) C[(int64_t)r * ldc + c] = f32_to_bf16_rne(rowwise_epilogue(mast[i][v], sa[sa_vec ? r : 0], sbc));
-    }
 }
 
 __global__ void fill_zero_bf16_kernel(uint16_t* C, int64_t ldc, int64_t M, int64_t N) {
@@ -355,6 +403,7 @@ __global__ void fill_zero_bf16_kernel(uint16_t* C, int64_t ldc, int64_t M, int64
 
 const char* variant_name(int v) {
   switch (v) {
+    case VAR_TILE_256x256: return "tile256x256";
     case VAR_TILE_256x128: return "tile256x128";
     case VAR_TILE_128x128: return "tile128x128";
     case VAR_DECODE_16: return "decode16";
@@ -366,6 +415,7 @@ const char* variant_name(int v) {
 
 bool variant_accepts(int v, int64_t M) {
   switch (v) {
+    case VAR_TILE_256x256:
     case VAR_TILE_256x128:
     case VAR_TILE_128x128: return true;
     case VAR_DECODE_16: return M <= 16;
@@ -375,21 +425,20 @@ bool variant_accepts(int v, int64_t M) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
-static hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
+template <int BM, int BN>
+static hipError_t launch_rowwise_tile(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
-  const int grid = tiles_m * tiles_n;
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE>), dim3(grid), dim3(256), 0, s, g.A,
-                     g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, g.sa,
-                     (int)(g.sa_kind == 1), static_cast<const float*>(g.sb),
-                     (int)(g.sb_kind == 2), tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_rowwise_kernel<BM, BN>), dim3(tiles_m * tiles_n), dim3(256), 0, s, g.A,
+                     g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
+                     static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
+                     static_cast<const float*>(g.sb), (int)(g.sb_kind == 2), tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-template <int TM>
+template <int TM, int D>
 static hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
   const int grid = (int)((g.N + 15) / 16);
-  hipLaunchKernelGGL((gemm_decode_kernel<TM>), dim3(grid), dim3(256), 0, s, g.A, g.lda, g.B,
+  hipLaunchKernelGGL((gemm_decode_kernel<TM, D>), dim3(grid), dim3(64), 0, s, g.A, g.lda, g.B,
                      g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
                      static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
                      static_cast<const float*>(g.sb), (int)(g.sb_kind == 2));
@@ -398,18 +447,27 @@ static hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
   switch (variant) {
-    case VAR_TILE_256x128: return launch_tile<256, 128, 2, 2, MODE_ROWWISE>(g, s);
-    case VAR_TILE_128x128: return launch_tile<128, 128, 2, 2, MODE_ROWWISE>(g, s);
-    case VAR_DECODE_16: return launch_decode<1>(g, s);
-    case VAR_DECODE_32: return launch_decode<2>(g, s);
-    case VAR_DECODE_64: return launch_decode<4>(g, s);
+    case VAR_TILE_256x256: return launch_rowwise_tile<256, 256>(g, s);
+    case VAR_TILE_256x128: return launch_rowwise_tile<256, 128>(g, s);
+    case VAR_TILE_128x128: return launch_rowwise_tile<128, 128>(g, s);
+    case VAR_DECODE_16: return launch_decode<1, 16>(g, s);
+    case VAR_DECODE_32: return launch_decode<2, 12>(g, s);
+    case VAR_DECODE_64: return launch_decode<4, 8>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemm_blockwise(const GemmArgs& g, hipStream_t s) {
-  if (g.sa_kind == 3) return launch_tile<128, 128, 2, 2, MODE_BLOCK_UE8M0>(g, s);
-  return launch_tile<128, 128, 2, 2, MODE_BLOCK_FP32>(g, s);
+  const int tiles_m = (int)((g.M + 127) / 128), tiles_n = (int)((g.N + 127) / 128);
+  if (g.sa_kind == 3)
+    hipLaunchKernelGGL((gemm_blockwise_kernel<true>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
+                       g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, g.sa,
+                       static_cast<const float*>(g.sb), tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_blockwise_kernel<false>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
+                       g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, g.sa,
+                       static_cast<const float*>(g.sb), tiles_m, tiles_n);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_zero_bf16(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s) {
