@@ -19,7 +19,7 @@ inline int pick_from_table(int64_t M, int64_t N, int64_t K) {
   if (M <= 32) return VAR_DECODE_32;
   if (M <= 64) return VAR_DECODE_64;
   if (M <= 1024 || N <= 1024) return VAR_TILE_128x128;
-  return VAR_TILE_256x256;
+  return VAR_TILE_128x256;
 }
 
 }  // namespace fp8sm

@@ -97,12 +97,16 @@ __device__ __attribute__((aligned(16))) uint8_t g_zero16[16];
 // kernel waits for exactly the stages it needs with wait_vmcnt.  lds_addr is
 // the wave-uniform LDS byte address of lane 0's destination; lane i writes
 // lds_addr + 16 i.
+// m0 is clobbered on purpose: these kernels use it for nothing else.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(lds_addr), "v"(g)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -115,10 +119,11 @@ __device__ __forceinline__ int swz16(int x) { return ((x >> 1) ^ (x >> 3)) & 3; 
 
 // ---------------------------------------------------------------------------
 // Rowwise tile kernel: BM x BN workgroup tile, 4 wavefronts in a 2 x 2 grid
-// (wave tile BM/2 x BN/2), 64-wide K chunks in a 4-slot LDS ring filled by
-// global->LDS DMA three chunks ahead, one barrier per chunk.
-template <int BM, int BN>
-__global__ __launch_bounds__(256, 1) void gemm_rowwise_kernel(
+// (wave tile BM/2 x BN/2), 64-wide K chunks in an NSLOT-slot LDS ring filled
+// by global->LDS DMA NSLOT-1 chunks ahead, one barrier per chunk.  OCC is the
+// number of workgroups meant to share a CU (their waits hide each other's).
+template <int BM, int BN, int NSLOT, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
     int sa_vec, const float* __restrict__ sb, int sb_vec, int tiles_m, int tiles_n) {
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(256, 1) void gemm_rowwise_kernel(
   constexpr int SLOT = ROWS * kChunk;          // bytes per ring slot
   constexpr int SEGS = SLOT / 1024;            // 1 KB segments per slot (16 rows each)
   constexpr int DPS = SEGS / 4;                // DMA instructions per thread per stage
-  constexpr int NSLOT = 4;
+  static_assert(NSLOT >= 2 && NSLOT <= 4, "ring depth");
   static_assert(SEGS % 4 == 0, "segments must split over the four wavefronts");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NSLOT * SLOT];
 
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(256, 1) void gemm_rowwise_kernel(
   }
   const int nkc = (K + kChunk - 1) / kChunk;
   auto issue = [&](int kc) {
-    const uint32_t slot = lds0 + (uint32_t)((kc & (NSLOT - 1)) * SLOT);
+    const uint32_t slot = lds0 + (uint32_t)((kc % NSLOT) * SLOT);
     const int64_t kb = (int64_t)kc * kChunk;
 #pragma unroll
     for (int i = 0; i < DPS; ++i) {
@@ -175,20 +180,19 @@ __global__ __launch_bounds__(256, 1) void gemm_rowwise_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0);
-  if (nkc > 1) issue(1);
-  if (nkc > 2) issue(2);
+  for (int c = 0; c < NSLOT - 1 && c < nkc; ++c) issue(c);
   for (int kc = 0; kc < nkc; ++kc) {
-    const int after = min(2, nkc - 1 - kc);  // stages issued after kc, still in flight
-    if (after == 2)
+    // stages issued behind chunk kc and still allowed in flight
+    const int after = min(NSLOT - 2, nkc - 1 - kc);
+    if (after >= 2)
       wait_vmcnt<2 * DPS>();
     else if (after == 1)
       wait_vmcnt<DPS>();
     else
       wait_vmcnt<0>();
     __syncthreads();  // chunk kc visible to all; slot of chunk kc-1 free
-    if (kc + 3 < nkc) issue(kc + 3);
-    const uint8_t* slot = lds + (kc & (NSLOT - 1)) * SLOT;
+    if (kc + NSLOT - 1 < nkc) issue(kc + NSLOT - 1);
+    const uint8_t* slot = lds + (kc % NSLOT) * SLOT;
     uint4 fa[TM], fb[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const uint4*>(slot + a_off + i * 16 * kChunk);
@@ -406,6 +410,7 @@ const char* variant_name(int v) {
     case VAR_TILE_256x256: return "tile256x256";
     case VAR_TILE_256x128: return "tile256x128";
     case VAR_TILE_128x128: return "tile128x128";
+    case VAR_TILE_128x256: return "tile128x256";
     case VAR_DECODE_16: return "decode16";
     case VAR_DECODE_32: return "decode32";
     case VAR_DECODE_64: return "decode64";
@@ -417,7 +422,8 @@ bool variant_accepts(int v, int64_t M) {
   switch (v) {
     case VAR_TILE_256x256:
     case VAR_TILE_256x128:
-    case VAR_TILE_128x128: return true;
+    case VAR_TILE_128x128:
+    case VAR_TILE_128x256: return true;
     case VAR_DECODE_16: return M <= 16;
     case VAR_DECODE_32: return M <= 32;
     case VAR_DECODE_64: return M <= 64;
@@ -425,10 +431,10 @@ bool variant_accepts(int v, int64_t M) {
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NSLOT, int OCC>
 static hipError_t launch_rowwise_tile(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_rowwise_kernel<BM, BN>), dim3(tiles_m * tiles_n), dim3(256), 0, s, g.A,
+  hipLaunchKernelGGL((gemm_rowwise_kernel<BM, BN, NSLOT, OCC>), dim3(tiles_m * tiles_n), dim3(256), 0, s, g.A,
                      g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
                      static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
                      static_cast<const float*>(g.sb), (int)(g.sb_kind == 2), tiles_m, tiles_n);
@@ -447,9 +453,10 @@ static hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
   switch (variant) {
-    case VAR_TILE_256x256: return launch_rowwise_tile<256, 256>(g, s);
-    case VAR_TILE_256x128: return launch_rowwise_tile<256, 128>(g, s);
-    case VAR_TILE_128x128: return launch_rowwise_tile<128, 128>(g, s);
+    case VAR_TILE_256x256: return launch_rowwise_tile<256, 256, 4, 1>(g, s);
+    case VAR_TILE_256x128: return launch_rowwise_tile<256, 128, 3, 2>(g, s);
+    case VAR_TILE_128x128: return launch_rowwise_tile<128, 128, 4, 2>(g, s);
+    case VAR_TILE_128x256: return launch_rowwise_tile<128, 256, 3, 2>(g, s);
     case VAR_DECODE_16: return launch_decode<1, 16>(g, s);
     case VAR_DECODE_32: return launch_decode<2, 12>(g, s);
     case VAR_DECODE_64: return launch_decode<4, 8>(g, s);
