@@ -29,6 +29,23 @@ PEAK_BF16_MFMA = 2500.0     # TFLOP/s, dense
 PEAK_FP8_MFMA = 5000.0      # TFLOP/s, dense
 PEAK_HBM = 8000.0           # GB/s
 
+# HBM traffic of one QKV GEMM launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes, scaled by a plain-copy calibration (profiles/
+# gemm_rowwise_128x256_qkv_traffic.md).  Valid only for the gemm.hip source it
+# was measured on; reported as null once that file changes.
+TRAFFIC = {"gemm_src_sha256_prefix": "8dda0789fda686bc", "workload": "qkv",
+           "kernel": "tile128x256", "bytes": 2208e6 + 584.4e6}
+
+
+def measured_traffic(workload, variant):
+    import hashlib
+    src = os.path.join(ROOT, "column_scaled_gemm_amd", "csrc", "gemm.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if (h == TRAFFIC["gemm_src_sha256_prefix"] and workload == TRAFFIC["workload"]
+            and variant == TRAFFIC["kernel"]):
+        return TRAFFIC["bytes"]
+    return None
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -42,7 +59,21 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB three times (a known-size "
+                        "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "reads": n, "writes": n, "launches": 3}))
 
 
 def cpu_baseline(w, M, N, K, target_s):
@@ -74,6 +105,9 @@ def cpu_baseline(w, M, N, K, target_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU path is not part of this build.", file=sys.stderr)
@@ -145,7 +179,9 @@ def main():
                        fp8sm.pick_variant(M, N, K))},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 3),
                      "peak": PEAK_BF16_MFMA, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / PEAK_BF16_MFMA, 4), "traffic": None},
+                     "frac": round(gemm_tflops / PEAK_BF16_MFMA, 4),
+                     "traffic": measured_traffic(args.workload, fp8sm.variant_name(
+                         fp8sm.pick_variant(M, N, K)))},
         "fp8_peak_frac": round(gemm_tflops / PEAK_FP8_MFMA, 4),
         "gemm_us": round(gemm_ms * 1e3, 2),
         "quant_us_est": round(quant_ms * 1e3, 2),
