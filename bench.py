@@ -59,6 +59,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--suite", action="store_true",
+                   help="time every hot-path kernel on its own workload (one JSON line each)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB three times (a known-size "
                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -103,8 +105,125 @@ def cpu_baseline(w, M, N, K, target_s):
                       f"{N}x{K} weight ({t:.1f} s)"}
 
 
+def _time_launches(fn, reps, cold, stream):
+    """Mean duration (us) of fn() from HIP events around each launch; with
+    cold=True a 512 MiB buffer is rewritten before every launch so the
+    256 MB last-level cache cannot serve the inputs."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0") if cold else None
+    fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        if cold:
+            flush.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+
+
+def suite(reps):
+    """One JSON line per hot-path row: quant GB/s (cold), decode GEMM (cold),
+    rowwise and blockwise GEMM TFLOP/s (warm: compute-bound)."""
+    import torch
+    from column_scaled_gemm_amd import fp8sm, inputs
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = []
+
+    def emit(row, **kv):
+        d = {"row": row}
+        d.update(kv)
+        print(json.dumps(d), flush=True)
+        out.append(d)
+
+    # a1 / a5: per-token quant + rowwise GEMM on the H3 shapes
+    for name in ("qkv", "mlp_gateup_23216", "mlp_gateup_15760", "mlp_down"):
+        M, N, K = inputs.ROWWISE_SHAPES[name]
+        w = inputs.workload(name)
+        x = w.x.to(dev)
+        qb, sb = fp8sm.quant_group(w.w.to(dev), -1)
+        del w
+        qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sa = torch.empty((M, 1), dtype=torch.float32, device=dev)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us_q = _time_launches(lambda: fp8sm.quant_group(x, -1, q=qa, scales=sa, stream=stream),
+                              reps, True, stream)
+        qbytes = 2 * M * K + M * K + 4 * M
+        emit("a1 per-token quant", workload=f"{name} bf16[{M},{K}]", us=round(us_q, 2),
+             GBps=round(qbytes / us_q / 1e3, 1), hbm_frac=round(qbytes / us_q / 1e3 / PEAK_HBM, 3),
+             cache="cold")
+        us_g = _time_launches(lambda: fp8sm.scaled_mm(qa, qb, sa.reshape(-1), sb.reshape(-1),
+                                                      fp8sm.KIND_ROW, fp8sm.KIND_COL, c=c,
+                                                      stream=stream), max(3, reps // 2), False,
+                              stream)
+        tf = 2.0 * M * N * K / us_g / 1e6
+        emit("a5 rowwise GEMM", workload=f"{name} {M}x{K}x{N}", us=round(us_g, 1),
+             TFLOPs=round(tf, 1), bf16_peak_frac=round(tf / PEAK_BF16_MFMA, 4),
+             fp8_peak_frac=round(tf / PEAK_FP8_MFMA, 4),
+             variant=fp8sm.variant_name(fp8sm.pick_variant(M, N, K)))
+        del x, qb, sb, qa, sa, c
+        torch.cuda.empty_cache()
+
+    # a3 / a6: static quant + per-tensor decode GEMM
+    d = inputs.decode()
+    xs = torch.tensor([d.x_scale], dtype=torch.float32, device=dev)
+    x = d.x.to(dev)
+    for N in inputs.DECODE_NS:
+        ws = torch.tensor([d.w_scale[N]], dtype=torch.float32, device=dev)
+        qw = fp8sm.quant_static(d.w[N].to(dev), ws)
+        for M in inputs.DECODE_MS:
+            qx = torch.empty((M, inputs.DECODE_K), dtype=torch.uint8, device=dev)
+            c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            us_s = _time_launches(lambda: fp8sm.quant_static(x[:M], xs, q=qx, stream=stream), reps,
+                                  True, stream)
+            us_d = _time_launches(lambda: fp8sm.scaled_mm(qx, qw, xs, ws, fp8sm.KIND_TENSOR,
+                                                          fp8sm.KIND_TENSOR, c=c, stream=stream),
+                                  reps, True, stream)
+            byts = N * inputs.DECODE_K + M * inputs.DECODE_K + 2 * M * N
+            emit("a3 static quant", workload=f"bf16[{M},{inputs.DECODE_K}]", us=round(us_s, 2),
+                 cache="cold")
+            emit("a6 decode GEMM", workload=f"M={M} K={inputs.DECODE_K} N={N} per-tensor",
+                 us=round(us_d, 2), GBps=round(byts / us_d / 1e3, 1),
+                 hbm_frac=round(byts / us_d / 1e3 / PEAK_HBM, 3),
+                 TFLOPs=round(2.0 * M * N * inputs.DECODE_K / us_d / 1e6, 2), cache="cold",
+                 variant=fp8sm.variant_name(fp8sm.pick_variant(M, N, inputs.DECODE_K)))
+
+    # a4 / a7: fused SiLU-and-mul + 1x128 UE8M0 quant, blockwise GEMM
+    f = inputs.fused()
+    Mf, Kf, Nf = inputs.FUSED_M, inputs.FUSED_K, inputs.FUSED_N
+    qb, sbb = fp8sm.quant_weight_block128(f.w.to(dev))
+    for tag, xin in (("bf16", f.gu_bf16), ("fp16", f.gu_fp16)):
+        xg = xin.to(dev)
+        qa = torch.empty((Mf, Kf), dtype=torch.uint8, device=dev)
+        ea = torch.empty((Mf, Kf // 128), dtype=torch.uint8, device=dev)
+        us_f = _time_launches(lambda: fp8sm.quant_group(xg, 128, fp8sm.SCALE_UE8M0_BYTE,
+                                                        fuse_silu_mul=True, q=qa, scales=ea,
+                                                        stream=stream), reps, True, stream)
+        fbytes = 4 * Mf * Kf + Mf * Kf + Mf * Kf // 128
+        emit("a4 fused SiLU-mul + 1x128 UE8M0 quant", workload=f"{tag}[{Mf},{2 * Kf}]",
+             us=round(us_f, 2), GBps=round(fbytes / us_f / 1e3, 1),
+             hbm_frac=round(fbytes / us_f / 1e3 / PEAK_HBM, 3), cache="cold")
+        c = torch.empty((Mf, Nf), dtype=torch.bfloat16, device=dev)
+        us_b = _time_launches(lambda: fp8sm.scaled_mm(qa, qb, ea, sbb, fp8sm.KIND_GROUP128_UE8M0,
+                                                      fp8sm.KIND_BLOCK128, c=c, stream=stream),
+                              reps, False, stream)
+        tf = 2.0 * Mf * Nf * Kf / us_b / 1e6
+        emit("a7 blockwise GEMM", workload=f"{tag} {Mf}x{Kf}x{Nf}", us=round(us_b, 1),
+             TFLOPs=round(tf, 1), bf16_peak_frac=round(tf / PEAK_BF16_MFMA, 4))
+    return out
+
+
 def main():
     args = parse()
+    if args.suite:
+        suite(max(args.steps, 5))
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
