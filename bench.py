@@ -105,31 +105,55 @@ def cpu_baseline(w, M, N, K, target_s):
                       f"{N}x{K} weight ({t:.1f} s)"}
 
 
-def _time_launches(fn, reps, cold, stream):
-    """Mean duration (us) of fn() from HIP events around each launch; with
-    cold=True a 512 MiB buffer is rewritten before every launch so the
-    256 MB last-level cache cannot serve the inputs."""
+def _time_launches(fn, reps, nrot, stream, batches=3):
+    """Mean kernel duration (us) of fn(i), launched `reps` times back to back.
+
+    fn(i) launches on input set i % nrot; with nrot > 1 the sets together
+    exceed the 256 MB last-level cache, so every launch reads from HBM.
+    Each batch is queued behind a device read sized to outlast the host's
+    enqueueing (measured during warm-up), so the HIP events around the batch
+    see no host gaps; a batch whose enqueue still outlasted that read is
+    flagged.  Returns (median batch mean, host_bound)."""
     import torch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0") if cold else None
-    fn()
     torch.cuda.synchronize()
-    evs = []
-    for _ in range(reps):
-        if cold:
-            flush.fill_(1)
+    t0 = time.perf_counter()
+    for i in range(nrot):
+        fn(i)
+    per_call = (time.perf_counter() - t0) / nrot
+    torch.cuda.synchronize()
+    # a read at ~4 TB/s lasting 3x the batch's enqueue time, 256 MiB .. 6 GiB
+    nbytes = int(min(max(3 * reps * per_call * 4e12, 256 << 20), 6 << 30))
+    spacer = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    means, host_bound = [], False
+    for _ in range(batches):
+        s0 = torch.cuda.Event(enable_timing=True)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        spacer.amax()
         a.record(stream)
-        fn()
+        t0 = time.perf_counter()
+        for i in range(reps):
+            fn(i)
+        host_us = (time.perf_counter() - t0) * 1e6
         b.record(stream)
-        evs.append((a, b))
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+        torch.cuda.synchronize()
+        if host_us > s0.elapsed_time(a) * 1e3:
+            host_bound = True
+        means.append(a.elapsed_time(b) * 1e3 / reps)
+    del spacer
+    return sorted(means)[len(means) // 2], host_bound
+
+
+def _rotations(bytes_per_set, cold):
+    """Input sets needed so a cold batch never finds its inputs in cache."""
+    return max(1, -(-(640 << 20) // max(bytes_per_set, 1))) if cold else 1
 
 
 def suite(reps):
-    """One JSON line per hot-path row: quant GB/s (cold), decode GEMM (cold),
-    rowwise and blockwise GEMM TFLOP/s (warm: compute-bound)."""
+    """One JSON line per hot-path row.  Quant and decode rows are cold (each
+    launch reads its inputs from HBM); the rowwise and blockwise GEMMs, which
+    are compute-bound, are warm."""
     import torch
     from column_scaled_gemm_amd import fp8sm, inputs
     dev = torch.device("cuda:0")
@@ -146,76 +170,93 @@ def suite(reps):
     for name in ("qkv", "mlp_gateup_23216", "mlp_gateup_15760", "mlp_down"):
         M, N, K = inputs.ROWWISE_SHAPES[name]
         w = inputs.workload(name)
-        x = w.x.to(dev)
         qb, sb = fp8sm.quant_group(w.w.to(dev), -1)
+        nrot = _rotations(3 * M * K, True)
+        xs = [w.x.to(dev) for _ in range(nrot)]
         del w
-        qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
-        sa = torch.empty((M, 1), dtype=torch.float32, device=dev)
-        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        us_q = _time_launches(lambda: fp8sm.quant_group(x, -1, q=qa, scales=sa, stream=stream),
-                              reps, True, stream)
+        qas = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nrot)]
+        sas = [torch.empty((M, 1), dtype=torch.float32, device=dev) for _ in range(nrot)]
+        us_q, hb = _time_launches(
+            lambda i: fp8sm.quant_group(xs[i % nrot], -1, q=qas[i % nrot], scales=sas[i % nrot],
+                                        stream=stream), max(reps, nrot), nrot, stream)
         qbytes = 2 * M * K + M * K + 4 * M
         emit("a1 per-token quant", workload=f"{name} bf16[{M},{K}]", us=round(us_q, 2),
              GBps=round(qbytes / us_q / 1e3, 1), hbm_frac=round(qbytes / us_q / 1e3 / PEAK_HBM, 3),
-             cache="cold")
-        us_g = _time_launches(lambda: fp8sm.scaled_mm(qa, qb, sa.reshape(-1), sb.reshape(-1),
-                                                      fp8sm.KIND_ROW, fp8sm.KIND_COL, c=c,
-                                                      stream=stream), max(3, reps // 2), False,
-                              stream)
+             cache="cold", host_bound=hb)
+        qa, sa = qas[0], sas[0]
+        del xs, qas[1:], sas[1:]
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us_g, hb = _time_launches(
+            lambda i: fp8sm.scaled_mm(qa, qb, sa.reshape(-1), sb.reshape(-1), fp8sm.KIND_ROW,
+                                      fp8sm.KIND_COL, c=c, stream=stream),
+            max(3, reps // 2), 1, stream, batches=2)
         tf = 2.0 * M * N * K / us_g / 1e6
         emit("a5 rowwise GEMM", workload=f"{name} {M}x{K}x{N}", us=round(us_g, 1),
              TFLOPs=round(tf, 1), bf16_peak_frac=round(tf / PEAK_BF16_MFMA, 4),
-             fp8_peak_frac=round(tf / PEAK_FP8_MFMA, 4),
+             fp8_peak_frac=round(tf / PEAK_FP8_MFMA, 4), cache="warm",
              variant=fp8sm.variant_name(fp8sm.pick_variant(M, N, K)))
-        del x, qb, sb, qa, sa, c
+        del qa, sa, qas, sas, qb, sb, c
         torch.cuda.empty_cache()
 
     # a3 / a6: static quant + per-tensor decode GEMM
     d = inputs.decode()
-    xs = torch.tensor([d.x_scale], dtype=torch.float32, device=dev)
+    Kd = inputs.DECODE_K
+    xsc = torch.tensor([d.x_scale], dtype=torch.float32, device=dev)
     x = d.x.to(dev)
     for N in inputs.DECODE_NS:
         ws = torch.tensor([d.w_scale[N]], dtype=torch.float32, device=dev)
-        qw = fp8sm.quant_static(d.w[N].to(dev), ws)
+        qw0 = fp8sm.quant_static(d.w[N].to(dev), ws)
+        nrot = _rotations(N * Kd, True)
+        qws = [qw0] + [qw0.clone() for _ in range(nrot - 1)]
         for M in inputs.DECODE_MS:
-            qx = torch.empty((M, inputs.DECODE_K), dtype=torch.uint8, device=dev)
-            c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            us_s = _time_launches(lambda: fp8sm.quant_static(x[:M], xs, q=qx, stream=stream), reps,
-                                  True, stream)
-            us_d = _time_launches(lambda: fp8sm.scaled_mm(qx, qw, xs, ws, fp8sm.KIND_TENSOR,
-                                                          fp8sm.KIND_TENSOR, c=c, stream=stream),
-                                  reps, True, stream)
-            byts = N * inputs.DECODE_K + M * inputs.DECODE_K + 2 * M * N
-            emit("a3 static quant", workload=f"bf16[{M},{inputs.DECODE_K}]", us=round(us_s, 2),
-                 cache="cold")
-            emit("a6 decode GEMM", workload=f"M={M} K={inputs.DECODE_K} N={N} per-tensor",
+            qx = torch.empty((M, Kd), dtype=torch.uint8, device=dev)
+            cs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(nrot)]
+            us_s, hb_s = _time_launches(lambda i: fp8sm.quant_static(x[:M], xsc, q=qx, stream=stream),
+                                        max(reps, 20), 1, stream)
+            us_d, hb = _time_launches(
+                lambda i: fp8sm.scaled_mm(qx, qws[i % nrot], xsc, ws, fp8sm.KIND_TENSOR,
+                                          fp8sm.KIND_TENSOR, c=cs[i % nrot], stream=stream),
+                max(reps, nrot), nrot, stream)
+            byts = N * Kd + M * Kd + 2 * M * N
+            emit("a3 static quant", workload=f"bf16[{M},{Kd}]", us=round(us_s, 2), cache="warm",
+                 host_bound=hb_s)
+            emit("a6 decode GEMM", workload=f"M={M} K={Kd} N={N} per-tensor",
                  us=round(us_d, 2), GBps=round(byts / us_d / 1e3, 1),
                  hbm_frac=round(byts / us_d / 1e3 / PEAK_HBM, 3),
-                 TFLOPs=round(2.0 * M * N * inputs.DECODE_K / us_d / 1e6, 2), cache="cold",
-                 variant=fp8sm.variant_name(fp8sm.pick_variant(M, N, inputs.DECODE_K)))
+                 TFLOPs=round(2.0 * M * N * Kd / us_d / 1e6, 2), cache="cold", host_bound=hb,
+                 variant=fp8sm.variant_name(fp8sm.pick_variant(M, N, Kd)))
+        del qws, qw0, cs
+        torch.cuda.empty_cache()
 
     # a4 / a7: fused SiLU-and-mul + 1x128 UE8M0 quant, blockwise GEMM
     f = inputs.fused()
     Mf, Kf, Nf = inputs.FUSED_M, inputs.FUSED_K, inputs.FUSED_N
     qb, sbb = fp8sm.quant_weight_block128(f.w.to(dev))
     for tag, xin in (("bf16", f.gu_bf16), ("fp16", f.gu_fp16)):
-        xg = xin.to(dev)
-        qa = torch.empty((Mf, Kf), dtype=torch.uint8, device=dev)
-        ea = torch.empty((Mf, Kf // 128), dtype=torch.uint8, device=dev)
-        us_f = _time_launches(lambda: fp8sm.quant_group(xg, 128, fp8sm.SCALE_UE8M0_BYTE,
-                                                        fuse_silu_mul=True, q=qa, scales=ea,
-                                                        stream=stream), reps, True, stream)
+        nrot = _rotations(4 * Mf * Kf, True)
+        xgs = [xin.to(dev) for _ in range(nrot)]
+        qas = [torch.empty((Mf, Kf), dtype=torch.uint8, device=dev) for _ in range(nrot)]
+        eas = [torch.empty((Mf, Kf // 128), dtype=torch.uint8, device=dev) for _ in range(nrot)]
+        us_f, hb = _time_launches(
+            lambda i: fp8sm.quant_group(xgs[i % nrot], 128, fp8sm.SCALE_UE8M0_BYTE,
+                                        fuse_silu_mul=True, q=qas[i % nrot], scales=eas[i % nrot],
+                                        stream=stream), max(reps, nrot), nrot, stream)
         fbytes = 4 * Mf * Kf + Mf * Kf + Mf * Kf // 128
         emit("a4 fused SiLU-mul + 1x128 UE8M0 quant", workload=f"{tag}[{Mf},{2 * Kf}]",
              us=round(us_f, 2), GBps=round(fbytes / us_f / 1e3, 1),
-             hbm_frac=round(fbytes / us_f / 1e3 / PEAK_HBM, 3), cache="cold")
+             hbm_frac=round(fbytes / us_f / 1e3 / PEAK_HBM, 3), cache="cold", host_bound=hb)
+        qa, ea = qas[0], eas[0]
+        del xgs, qas, eas
         c = torch.empty((Mf, Nf), dtype=torch.bfloat16, device=dev)
-        us_b = _time_launches(lambda: fp8sm.scaled_mm(qa, qb, ea, sbb, fp8sm.KIND_GROUP128_UE8M0,
-                                                      fp8sm.KIND_BLOCK128, c=c, stream=stream),
-                              reps, False, stream)
+        us_b, hb = _time_launches(
+            lambda i: fp8sm.scaled_mm(qa, qb, ea, sbb, fp8sm.KIND_GROUP128_UE8M0,
+                                      fp8sm.KIND_BLOCK128, c=c, stream=stream),
+            max(reps, 5), 1, stream, batches=2)
         tf = 2.0 * Mf * Nf * Kf / us_b / 1e6
         emit("a7 blockwise GEMM", workload=f"{tag} {Mf}x{Kf}x{Nf}", us=round(us_b, 1),
-             TFLOPs=round(tf, 1), bf16_peak_frac=round(tf / PEAK_BF16_MFMA, 4))
+             TFLOPs=round(tf, 1), bf16_peak_frac=round(tf / PEAK_BF16_MFMA, 4), cache="warm")
+        del qa, ea, c
+        torch.cuda.empty_cache()
     return out
 
 

@@ -41,6 +41,31 @@ __device__ __forceinline__ bf16x8 widen_e4m3_x8(uint32_t d0, uint32_t d1) {
 
 // One canonical 64-wide chunk for TM x TN 16x16 output tiles: fa/fb hold each
 // lane's 16 bytes (k = 16g .. 16g+15 of the chunk) per row / column subtile.
+// Rowwise form: B is the instruction's first operand, so acc[i][j] holds the
+// transposed tile -- lane l has row 16i + l%16 and the four consecutive
+// columns 16j + 4(l/16) .. +3, which the epilogue stores as one 8-byte write.
+template <int TM, int TN>
+__device__ __forceinline__ void mma_chunk64_bt(const uint4 (&fa)[TM], const uint4 (&fb)[TN],
+                                               f32x4 (&acc)[TM][TN]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    bf16x8 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      a[i] = s == 0 ? widen_e4m3_x8(fa[i].x, fa[i].y) : widen_e4m3_x8(fa[i].z, fa[i].w);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      b[j] = s == 0 ? widen_e4m3_x8(fb[j].x, fb[j].y) : widen_e4m3_x8(fb[j].z, fb[j].w);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Same chunk with A as the first operand (blockwise kernel: lane l has column
+// 16j + l%16 and rows 16i + 4(l/16) .. +3).
 template <int TM, int TN>
 __device__ __forceinline__ void mma_chunk64(const uint4 (&fa)[TM], const uint4 (&fb)[TN],
                                             f32x4 (&acc)[TM][TN]) {
@@ -70,6 +95,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ float rowwise_epilogue(float acc, float sa, float sb) {
   const float v = acc * sa;
   return v * sb;
+}
+
+// Scale and store one lane's four consecutive outputs of row r (columns c..c+3,
+// c a multiple of 4; N % 8 == 0 so all four are in range when c < N).
+__device__ __forceinline__ void store_row4(uint16_t* __restrict__ C, int64_t ldc, int r, int c,
+                                           const f32x4& acc, float sar,
+                                           const float* __restrict__ sb, int sb_vec) {
+  float sbv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) sbv[v] = sb[sb_vec ? c + v : 0];
+  const uint32_t lo = (uint32_t)f32_to_bf16_rne(rowwise_epilogue(acc[0], sar, sbv[0])) |
+                      ((uint32_t)f32_to_bf16_rne(rowwise_epilogue(acc[1], sar, sbv[1])) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16_rne(rowwise_epilogue(acc[2], sar, sbv[2])) |
+                      ((uint32_t)f32_to_bf16_rne(rowwise_epilogue(acc[3], sar, sbv[3])) << 16);
+  *reinterpret_cast<uint2*>(C + (int64_t)r * ldc + c) = make_uint2(lo, hi);
 }
 
 // Hardware places consecutive workgroups on the 8 XCDs in turn; give each XCD
@@ -198,21 +238,18 @@ __global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
     for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const uint4*>(slot + a_off + i * 16 * kChunk);
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const uint4*>(slot + b_off + j * 16 * kChunk);
-    mma_chunk64<TM, TN>(fa, fb, acc);
+    mma_chunk64_bt<TM, TN>(fa, fb, acc);
   }
 
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int c = n0 + wn * (BN / 2) + 16 * j + r16;
-    const float sbc = sb[sb_vec ? min(c, N - 1) : 0];
+  for (int i = 0; i < TM; ++i) {
+    const int r = m0 + wm * (BM / 2) + 16 * i + r16;
+    if (r >= M) continue;
+    const float sar = sa[sa_vec ? r : 0];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = m0 + wm * (BM / 2) + 16 * i + 4 * g + v;
-        if (r < M && c < N)
-          C[(int64_t)r * ldc + c] = f32_to_bf16_rne(rowwise_epilogue(acc[i][j][v], sa[sa_vec ? r : 0], sbc));
-      }
+    for (int j = 0; j < TN; ++j) {
+      const int c = n0 + wn * (BN / 2) + 16 * j + 4 * g;
+      if (c < N) store_row4(C, ldc, r, c, acc[i][j], sar, sb, sb_vec);
     }
   }
 }
