@@ -15,6 +15,11 @@
 // 8-byte stores that are contiguous across the wavefront.
 #include "device_common.h"
 #include "launch.h"
+#include "silu_table.h"
+
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
 
 namespace fp8sm {
 
@@ -45,14 +50,42 @@ __device__ __forceinline__ void store_scale(void* scales, int64_t idx, float v, 
   }
 }
 
+// y = silu(gate) * up in fp32 (fused) or the widened input; `tab` is the
+// workgroup's silu table (fused only).
 template <bool F16, bool FUSED>
-__device__ __forceinline__ void load_values(const uint4 gv, const uint4 uv, float* y) {
+__device__ __forceinline__ void load_values(const uint4 gv, const uint4 uv, float* y,
+                                            const void* tab) {
   widen8<F16>(gv, y);
   if constexpr (FUSED) {
     float u[8];
     widen8<F16>(uv, u);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = silu_f32(y[i]) * u[i];
+    for (int i = 0; i < 8; ++i) y[i] = SiluTable<F16>::lookup(tab, y[i]) * u[i];
+  }
+}
+
+// Quantize one 1x128 group held by a 16-lane quarter (8 values per lane) and
+// store its codes and scale.
+template <int FMT>
+__device__ __forceinline__ void quant_group128(float* y, int l16, int64_t row, int64_t grp,
+                                               uint8_t* __restrict__ q, int64_t ld_q,
+                                               void* __restrict__ scales, int64_t G,
+                                               int mn_major, int64_t mpad) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
+  amax = group_max<16>(amax);
+  float sval;
+  int eb;
+  const float mult = group_multiplier<FMT>(amax, &sval, &eb);
+  if (row >= 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = y[i] * mult;
+    *reinterpret_cast<uint2*>(q + row * ld_q + grp * 128 + l16 * 8) = to_e4m3_x8(y);
+    if (l16 == 0) {
+      const int64_t idx = mn_major ? grp * mpad + row : row * G + grp;
+      store_scale<FMT>(scales, idx, sval, eb);
+    }
   }
 }
 
@@ -60,53 +93,112 @@ __device__ __forceinline__ void load_values(const uint4 gv, const uint4 uv, floa
 // 1x128 groups.  A 16-lane quarter of a wavefront owns one group (16 lanes x 8
 // values); a wavefront owns kQuads x 4 consecutive groups of the flattened
 // (row, group) index, issuing all its loads before any arithmetic.
-template <bool F16, bool FUSED, int FMT>
+constexpr int kQuads = 4;
+
+template <bool F16, int FMT>
 __global__ __launch_bounds__(256) void quant_g128_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t G, int64_t K, int64_t ld_x,
+    const uint16_t* __restrict__ x, int64_t M, int64_t G, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, int mn_major,
     int64_t mpad) {
-  constexpr int kQuads = 4;
   const int lane = threadIdx.x & 63;
   const int quarter = lane >> 4;
   const int l16 = lane & 15;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t total = M * G;
-  uint4 gv[kQuads], uv[kQuads];
+  uint4 gv[kQuads];
   int64_t row[kQuads], grp[kQuads];
 #pragma unroll
   for (int u = 0; u < kQuads; ++u) {
     const int64_t gid = (wave * kQuads + u) * 4 + quarter;
     row[u] = -1;
+    grp[u] = 0;
     gv[u] = make_uint4(0, 0, 0, 0);
-    uv[u] = make_uint4(0, 0, 0, 0);
     if (gid < total) {
       row[u] = gid / G;
       grp[u] = gid - row[u] * G;
-      const uint16_t* src = x + row[u] * ld_x + grp[u] * 128 + l16 * 8;
-      gv[u] = load_stream16(src);
-      if constexpr (FUSED) uv[u] = load_stream16(src + K);
+      gv[u] = load_stream16(x + row[u] * ld_x + grp[u] * 128 + l16 * 8);
     }
   }
 #pragma unroll
   for (int u = 0; u < kQuads; ++u) {
     float y[8];
-    load_values<F16, FUSED>(gv[u], uv[u], y);
-    float amax = 0.0f;
+    widen8<F16>(gv[u], y);
+    quant_group128<FMT>(y, l16, row[u], grp[u], q, ld_q, scales, G, mn_major, mpad);
+  }
+}
+
+// Fused SiLU-and-mul + 1x128 groups: one 1024-thread workgroup per CU builds
+// the silu table in LDS, then its 16 wavefronts walk the flattened
+// (row, group) space 16 groups (kQuads x 4 quarters) per step, loading the
+// next step while converting the current one.  A fused row is [gate | up],
+// each K wide.  M and G are at most 2^30 (checked at the boundary), so rows
+// and groups fit in int.  Each lane keeps a (row, group) cursor per quad and
+// advances it without division; loads past the last row read the last row
+// and are never stored, so the loads are branch-free and the compiler's
+// wait counts leave the next step's loads in flight.
+struct G128Step {
+  uint4 g[kQuads], u[kQuads];
+  int row[kQuads], grp[kQuads];  // row = -1: past the end
+};
+
+template <bool F16, int FMT>
+__global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
+    const uint16_t* __restrict__ x, int M, int G, int64_t K, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, int mn_major,
+    int64_t mpad) {
+  __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
+  const int lane = threadIdx.x & 63;
+  const int quarter = lane >> 4;
+  const int l16 = lane & 15;
+  const int64_t total = (int64_t)M * G;
+  // step w covers flattened groups 16 w .. 16 w + 15; a wavefront's steps are
+  // nw apart, i.e. each cursor moves by 16 nw groups = (drow, dgrp)
+  const int64_t nw = (int64_t)gridDim.x * 16;
+  int64_t w = (int64_t)blockIdx.x * 16 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int drow = (int)(nw * 16 / G), dgrp = (int)(nw * 16 - (int64_t)drow * G);
+  int cr[kQuads], cc[kQuads];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
-    amax = group_max<16>(amax);
-    float sval;
-    int eb;
-    const float mult = group_multiplier<FMT>(amax, &sval, &eb);
-    if (row[u] >= 0) {
+  for (int u = 0; u < kQuads; ++u) {
+    const int64_t gid = w * 16 + 4 * u + quarter;
+    cr[u] = (int)(gid / G);
+    cc[u] = (int)(gid - (int64_t)cr[u] * G);
+  }
+  auto fetch = [&](G128Step& st) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = y[i] * mult;
-      *reinterpret_cast<uint2*>(q + row[u] * ld_q + grp[u] * 128 + l16 * 8) = to_e4m3_x8(y);
-      if (l16 == 0) {
-        const int64_t idx = mn_major ? grp[u] * mpad + row[u] : row[u] * G + grp[u];
-        store_scale<FMT>(scales, idx, sval, eb);
-      }
+    for (int u = 0; u < kQuads; ++u) {
+      const int r = min(cr[u], M - 1);
+      const uint16_t* src = x + (int64_t)r * ld_x + (int64_t)cc[u] * 128 + l16 * 8;
+      st.g[u] = load_stream16(src);
+      st.u[u] = load_stream16(src + K);
+      st.row[u] = cr[u] < M ? cr[u] : -1;
+      st.grp[u] = cc[u];
+      // advance the cursor to the wavefront's next step
+      int c = cc[u] + dgrp, rr = cr[u] + drow;
+      const bool wrap = c >= G;
+      cc[u] = wrap ? c - G : c;
+      cr[u] = wrap ? rr + 1 : rr;
     }
+  };
+  auto convert = [&](const G128Step& st) {
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+      float y[8];
+      load_values<F16, true>(st.g[u], st.u[u], y, tab);
+      quant_group128<FMT>(y, l16, st.row[u], st.grp[u], q, ld_q, scales, G, mn_major, mpad);
+    }
+  };
+  G128Step a, b;
+  fetch(a);  // the first loads overlap the table build
+  SiluTable<F16>::build(tab, threadIdx.x, 1024);
+  __syncthreads();
+  while (w * 16 < total) {
+    w += nw;
+    fetch(b);
+    convert(a);
+    if (w * 16 >= total) break;
+    w += nw;
+    fetch(a);
+    convert(b);
   }
 }
 
@@ -156,24 +248,22 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
   if (lane == 0) store_scale<FMT>(scales, row, sval, eb);
 }
 
-// Per token, any K and the fused form: two passes over the row (the second
-// pass re-reads it from L2) so no register budget limits K.
+// Per token, any K: two passes over the row (the second pass re-reads it from
+// L2) so no register budget limits K.  The row pass is shared by the plain
+// kernel below (one wavefront per row) and the fused one (persistent
+// 1024-thread workgroups that hold the silu table).
 template <bool F16, bool FUSED, int FMT>
-__global__ __launch_bounds__(256) void quant_token_2pass_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
+__device__ __forceinline__ void quant_row_2pass(const uint16_t* __restrict__ xr, int64_t K,
+                                                uint8_t* __restrict__ qr, void* __restrict__ scales,
+                                                int64_t row, int lane, const void* tab) {
   const int64_t nch = K >> 3;
-  const uint16_t* xr = x + row * ld_x;
   float amax = 0.0f;
   for (int64_t c = lane; c < nch; c += 64) {
     const uint4 g = *reinterpret_cast<const uint4*>(xr + c * 8);
     uint4 u = make_uint4(0, 0, 0, 0);
     if constexpr (FUSED) u = *reinterpret_cast<const uint4*>(xr + K + c * 8);
     float y[8];
-    load_values<F16, FUSED>(g, u, y);
+    load_values<F16, FUSED>(g, u, y, tab);
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(y[j]));
   }
@@ -181,18 +271,40 @@ __global__ __launch_bounds__(256) void quant_token_2pass_kernel(
   float sval;
   int eb;
   const float mult = group_multiplier<FMT>(amax, &sval, &eb);
-  uint8_t* qr = q + row * ld_q;
   for (int64_t c = lane; c < nch; c += 64) {
     const uint4 g = *reinterpret_cast<const uint4*>(xr + c * 8);
     uint4 u = make_uint4(0, 0, 0, 0);
     if constexpr (FUSED) u = *reinterpret_cast<const uint4*>(xr + K + c * 8);
     float y[8];
-    load_values<F16, FUSED>(g, u, y);
+    load_values<F16, FUSED>(g, u, y, tab);
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
     *reinterpret_cast<uint2*>(qr + c * 8) = to_e4m3_x8(y);
   }
   if (lane == 0) store_scale<FMT>(scales, row, sval, eb);
+}
+
+template <bool F16, int FMT>
+__global__ __launch_bounds__(256) void quant_token_2pass_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;  // whole wavefront; the kernel has no barrier
+  quant_row_2pass<F16, false, FMT>(x + row * ld_x, K, q + row * ld_q, scales, row,
+                                   threadIdx.x & 63, nullptr);
+}
+
+template <bool F16, int FMT>
+__global__ __launch_bounds__(1024) void quant_token_fused_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
+  SiluTable<F16>::build(tab, threadIdx.x, 1024);
+  __syncthreads();
+  for (int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6); row < M;
+       row += (int64_t)gridDim.x * 16)
+    quant_row_2pass<F16, true, FMT>(x + row * ld_x, K, q + row * ld_q, scales, row,
+                                    threadIdx.x & 63, tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -218,11 +330,15 @@ __global__ __launch_bounds__(256) void quant_static_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// The fused product alone in fp32 (same silu_f32 as the fused quant).
+// The fused product alone in fp32, through the same table and lookup as the
+// fused quant kernels.
 template <bool F16>
-__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                       int64_t K, int64_t ld_x,
-                                                       float* __restrict__ y, int64_t ld_y) {
+__global__ __launch_bounds__(1024) void silu_mul_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                        int64_t K, int64_t ld_x,
+                                                        float* __restrict__ y, int64_t ld_y) {
+  __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
+  SiluTable<F16>::build(tab, threadIdx.x, 1024);
+  __syncthreads();
   const int64_t nch = K >> 3;
   const int64_t total = M * nch;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -231,7 +347,7 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
     const uint16_t* src = x + r * ld_x + c * 8;
     float v[8];
     load_values<F16, true>(*reinterpret_cast<const uint4*>(src),
-                           *reinterpret_cast<const uint4*>(src + K), v);
+                           *reinterpret_cast<const uint4*>(src + K), v, tab);
     float4* dst = reinterpret_cast<float4*>(y + r * ld_y + c * 8);
     dst[0] = make_float4(v[0], v[1], v[2], v[3]);
     dst[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -291,69 +407,92 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(
 // ---------------------------------------------------------------------------
 // host-side launchers
 
-template <bool F16, bool FUSED>
-static hipError_t launch_g128_fmt(int fmt, const QuantArgs& a, hipStream_t s) {
-  const int64_t G = a.K / 128;
-  const int64_t waves = (a.M * G + 15) / 16;
-  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+// Runs f(std::integral_constant<int, FMT>) for the runtime scale format.
+template <typename Fn>
+static hipError_t with_fmt(int fmt, Fn&& f) {
   switch (fmt) {
-    case FMT_FP32:
-      hipLaunchKernelGGL((quant_g128_kernel<F16, FUSED, FMT_FP32>), grid, block, 0, s, x, a.M, G,
-                         a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad);
-      break;
-    case FMT_UE8M0_FP32:
-      hipLaunchKernelGGL((quant_g128_kernel<F16, FUSED, FMT_UE8M0_FP32>), grid, block, 0, s, x,
-                         a.M, G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad);
-      break;
-    default:
-      hipLaunchKernelGGL((quant_g128_kernel<F16, FUSED, FMT_UE8M0_BYTE>), grid, block, 0, s, x,
-                         a.M, G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad);
-      break;
+    case FMT_FP32: f(std::integral_constant<int, FMT_FP32>{}); break;
+    case FMT_UE8M0_FP32: f(std::integral_constant<int, FMT_UE8M0_FP32>{}); break;
+    default: f(std::integral_constant<int, FMT_UE8M0_BYTE>{}); break;
   }
   return hipGetLastError();
+}
+
+// Compute units of the current device (persistent fused kernels launch one
+// 1024-thread workgroup per CU).
+static int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+static unsigned persistent_blocks(int64_t work_per_block_units, int64_t units) {
+  const int64_t need = (units + work_per_block_units - 1) / work_per_block_units;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(need, cu_count()));
+}
+
+template <bool F16>
+static hipError_t launch_g128(int fmt, const QuantArgs& a, hipStream_t s) {
+  const int64_t G = a.K / 128;
+  const int64_t waves = (a.M * G + 15) / 16;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  return with_fmt(fmt, [&](auto f) {
+    constexpr int FMT = decltype(f)::value;
+    hipLaunchKernelGGL((quant_g128_kernel<F16, FMT>), dim3((unsigned)((waves + 3) / 4)),
+                       dim3(256), 0, s, x, a.M, G, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major,
+                       a.mpad);
+  });
+}
+
+template <bool F16>
+static hipError_t launch_g128_fused(int fmt, const QuantArgs& a, hipStream_t s) {
+  const int64_t G = a.K / 128;
+  const unsigned blocks = persistent_blocks(16 * 16, a.M * G);  // 16 waves x 16 groups
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  return with_fmt(fmt, [&](auto f) {
+    constexpr int FMT = decltype(f)::value;
+    hipLaunchKernelGGL((quant_g128_fused_kernel<F16, FMT>), dim3(blocks), dim3(1024), 0, s, x,
+                       (int)a.M, (int)G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad);
+  });
 }
 
 template <bool F16, int NC>
 static hipError_t launch_token_nc(int fmt, const QuantArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.M + 3) / 4)), block(256);
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  switch (fmt) {
-    case FMT_FP32:
-      hipLaunchKernelGGL((quant_token_kernel<F16, NC, FMT_FP32>), grid, block, 0, s, x, a.M, a.K,
-                         a.ld_x, a.q, a.ld_q, a.scales);
-      break;
-    case FMT_UE8M0_FP32:
-      hipLaunchKernelGGL((quant_token_kernel<F16, NC, FMT_UE8M0_FP32>), grid, block, 0, s, x, a.M,
-                         a.K, a.ld_x, a.q, a.ld_q, a.scales);
-      break;
-    default:
-      hipLaunchKernelGGL((quant_token_kernel<F16, NC, FMT_UE8M0_BYTE>), grid, block, 0, s, x, a.M,
-                         a.K, a.ld_x, a.q, a.ld_q, a.scales);
-      break;
-  }
-  return hipGetLastError();
+  return with_fmt(fmt, [&](auto f) {
+    constexpr int FMT = decltype(f)::value;
+    hipLaunchKernelGGL((quant_token_kernel<F16, NC, FMT>), dim3((unsigned)((a.M + 3) / 4)),
+                       dim3(256), 0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+  });
 }
 
-template <bool F16, bool FUSED>
+template <bool F16>
 static hipError_t launch_token_2pass(int fmt, const QuantArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.M + 3) / 4)), block(256);
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  switch (fmt) {
-    case FMT_FP32:
-      hipLaunchKernelGGL((quant_token_2pass_kernel<F16, FUSED, FMT_FP32>), grid, block, 0, s, x,
-                         a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
-      break;
-    case FMT_UE8M0_FP32:
-      hipLaunchKernelGGL((quant_token_2pass_kernel<F16, FUSED, FMT_UE8M0_FP32>), grid, block, 0,
-                         s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
-      break;
-    default:
-      hipLaunchKernelGGL((quant_token_2pass_kernel<F16, FUSED, FMT_UE8M0_BYTE>), grid, block, 0,
-                         s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
-      break;
-  }
-  return hipGetLastError();
+  return with_fmt(fmt, [&](auto f) {
+    constexpr int FMT = decltype(f)::value;
+    hipLaunchKernelGGL((quant_token_2pass_kernel<F16, FMT>), dim3((unsigned)((a.M + 3) / 4)),
+                       dim3(256), 0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+  });
+}
+
+template <bool F16>
+static hipError_t launch_token_fused(int fmt, const QuantArgs& a, hipStream_t s) {
+  const unsigned blocks = persistent_blocks(16, a.M);  // one row per wavefront
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  return with_fmt(fmt, [&](auto f) {
+    constexpr int FMT = decltype(f)::value;
+    hipLaunchKernelGGL((quant_token_fused_kernel<F16, FMT>), dim3(blocks), dim3(1024), 0, s, x,
+                       a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+  });
 }
 
 template <bool F16>
@@ -367,21 +506,20 @@ static hipError_t launch_token(int fmt, const QuantArgs& a, hipStream_t s) {
   if (per_lane <= 16) return launch_token_nc<F16, 16>(fmt, a, s);
   if (per_lane <= 24) return launch_token_nc<F16, 24>(fmt, a, s);
   if (per_lane <= 32) return launch_token_nc<F16, 32>(fmt, a, s);
-  return launch_token_2pass<F16, false>(fmt, a, s);
+  return launch_token_2pass<F16>(fmt, a, s);
 }
 
 hipError_t launch_quant_group(const QuantArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   const bool per_token = a.group == a.K;
   if (per_token) {
-    if (a.fused) return a.f16 ? launch_token_2pass<true, true>(a.fmt, a, s)
-                              : launch_token_2pass<false, true>(a.fmt, a, s);
+    if (a.fused) return a.f16 ? launch_token_fused<true>(a.fmt, a, s)
+                              : launch_token_fused<false>(a.fmt, a, s);
     return a.f16 ? launch_token<true>(a.fmt, a, s) : launch_token<false>(a.fmt, a, s);
   }
-  if (a.fused) return a.f16 ? launch_g128_fmt<true, true>(a.fmt, a, s)
-                            : launch_g128_fmt<false, true>(a.fmt, a, s);
-  return a.f16 ? launch_g128_fmt<true, false>(a.fmt, a, s)
-               : launch_g128_fmt<false, false>(a.fmt, a, s);
+  if (a.fused) return a.f16 ? launch_g128_fused<true>(a.fmt, a, s)
+                            : launch_g128_fused<false>(a.fmt, a, s);
+  return a.f16 ? launch_g128<true>(a.fmt, a, s) : launch_g128<false>(a.fmt, a, s);
 }
 
 hipError_t launch_quant_static(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x,
@@ -403,15 +541,14 @@ hipError_t launch_quant_static(const void* x, bool f16, int64_t M, int64_t K, in
 hipError_t launch_silu_mul(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x, float* y,
                            int64_t ld_y, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  int64_t blocks = (M * (K / 8) + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  const unsigned blocks = persistent_blocks(1024, M * (K / 8));
   const uint16_t* xx = static_cast<const uint16_t*>(x);
   if (f16)
-    hipLaunchKernelGGL((silu_mul_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, xx, M, K,
-                       ld_x, y, ld_y);
+    hipLaunchKernelGGL((silu_mul_kernel<true>), dim3(blocks), dim3(1024), 0, s, xx, M, K, ld_x, y,
+                       ld_y);
   else
-    hipLaunchKernelGGL((silu_mul_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, xx, M,
-                       K, ld_x, y, ld_y);
+    hipLaunchKernelGGL((silu_mul_kernel<false>), dim3(blocks), dim3(1024), 0, s, xx, M, K, ld_x,
+                       y, ld_y);
   return hipGetLastError();
 }
 
