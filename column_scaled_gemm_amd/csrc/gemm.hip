@@ -23,7 +23,12 @@
 //
 // Blockwise (1x128 activation groups x 128x128 weight blocks): a fresh fp32
 // partial per 128-wide K block, multiplied by sa[m,kb] * sb[n/128,kb] in fp64
-// and accumulated in an fp64 master; bf16 of the master at the end.
+// and accumulated in an fp64 master; bf16 of the master at the end.  With
+// UE8M0 activation scales the power of two sa[m,kb] is applied exactly while
+// widening A, so only the weight scale, one per tile and block, multiplies
+// the partial; that kernel uses v_mfma_f32_32x32x16_bf16 (near-fp32 sums,
+// measured like the 16x16 instruction) and its own K order, since blockwise
+// rows are compared with the oracle, not with the rowwise variants.
 #include "device_common.h"
 #include "launch.h"
 
@@ -36,6 +41,14 @@ __device__ __forceinline__ bf16x8 widen_e4m3_x8(uint32_t d0, uint32_t d1) {
   const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
   const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
   const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ bf16x8 widen_e4m3_x8_scaled(uint32_t d0, uint32_t d1, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true);
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
@@ -84,6 +97,55 @@ __device__ __forceinline__ void mma_chunk64(const uint4 (&fa)[TM], const uint4 (
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// 32 x 32 chunk of the UE8M0 blockwise path.  A 64-wide K chunk is four
+// v_mfma_f32_32x32x16_bf16 steps.  Lane half
+// h = lane / 32 holds k = 32h .. 32h + 31 of its row (two 16-byte pieces),
+// and step s multiplies k = 32h + 8s .. 32h + 8s + 7 of both halves.  B is the
+// instruction's first operand, so in a 32 x 32 output subtile lane l holds
+// output row l % 32 and the columns 8v + 4h .. 8v + 4h + 3 in
+// acc[4v .. 4v + 3], v = 0..3, which the epilogue stores as 8-byte writes.
+struct Frag32 {
+  uint4 q[2];  // a lane's 32 bytes of one row of a chunk
+};
+
+template <bool SCALED, int S>
+__device__ __forceinline__ bf16x8 widen_step(const Frag32& f, float scale) {
+  const uint4 v = f.q[S >> 1];
+  const uint32_t d0 = (S & 1) ? v.z : v.x, d1 = (S & 1) ? v.w : v.y;
+  if constexpr (SCALED) return widen_e4m3_x8_scaled(d0, d1, scale);
+  return widen_e4m3_x8(d0, d1);
+}
+
+template <int TM, int TN, bool SCALED, int S>
+__device__ __forceinline__ void mma32_step(const Frag32 (&fa)[TM], const float (&asc)[TM],
+                                           const Frag32 (&fb)[TN], f32x16 (&acc)[TM][TN]) {
+  bf16x8 a[TM], b[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a[i] = widen_step<SCALED, S>(fa[i], asc[i]);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b[j] = widen_step<false, S>(fb[j], 1.0f);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+}
+
+// With SCALED, A row subtile i is widened times asc[i], a power of two: the
+// widen is exact (every finite E4M3 value times 2^e, |e| <= 100, is a bf16
+// value), so products and fp32 sums are the unscaled ones times 2^e.
+template <int TM, int TN, bool SCALED>
+__device__ __forceinline__ void mma32_chunk(const Frag32 (&fa)[TM], const float (&asc)[TM],
+                                            const Frag32 (&fb)[TN], f32x16 (&acc)[TM][TN]) {
+  mma32_step<TM, TN, SCALED, 0>(fa, asc, fb, acc);
+  mma32_step<TM, TN, SCALED, 1>(fa, asc, fb, acc);
+  mma32_step<TM, TN, SCALED, 2>(fa, asc, fb, acc);
+  mma32_step<TM, TN, SCALED, 3>(fa, asc, fb, acc);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -156,6 +218,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // at position c ^ swz16(r mod 16).  A 16-lane group reading the same chunk of
 // 16 consecutive rows (and any 8-lane phase of it) then hits distinct banks.
 __device__ __forceinline__ int swz16(int x) { return ((x >> 1) ^ (x >> 3)) & 3; }
+
+// LDS byte offset of piece q (0, 1) of this lane's 32 bytes within a 64-byte
+// chunk row of a 32-row subtile (subtiles start at multiples of 16 rows).
+// Each 8-lane phase of a 16-byte read then covers 8 consecutive rows and hits
+// 8 distinct bank groups.
+__device__ __forceinline__ int frag32_off(int lane, int q) {
+  return (lane & 31) * kChunk + ((((lane >> 5) * 2 + q) ^ swz16(lane & 15)) << 4);
+}
 
 // ---------------------------------------------------------------------------
 // Rowwise tile kernel: BM x BN workgroup tile, 4 wavefronts in a 2 x 2 grid
@@ -251,6 +321,175 @@ __global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
       const int c = n0 + wn * (BN / 2) + 16 * j + 4 * g;
       if (c < N) store_row4(C, ldc, r, c, acc[i][j], sar, sb, sb_vec);
     }
+  }
+}
+
+// fp64 -> bf16 with one rounding (nearest even) for results in the bf16
+// normal range; smaller magnitudes, zeros and NaN go through fp32.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  if (!(fabs(x) >= 0x1p-126)) return f32_to_bf16_rne((float)x);
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  u += ((uint64_t)1 << 44) - 1 + ((u >> 45) & 1);  // round to 8 significant bits
+  u &= ~(((uint64_t)1 << 45) - 1);
+  return f32_to_bf16_rne((float)__longlong_as_double((long long)u));  // exact now
+}
+
+// ---------------------------------------------------------------------------
+// Blockwise kernel for 1x128 UE8M0 activation groups and 128x128 fp32 weight
+// blocks.  Same ring, chunk order and B-first layout as the rowwise kernel,
+// with a 128 x 128 tile (wavefronts of 64 x 64).  The activation scale
+// 2^(byte - 127) is applied exactly in the widen, so each 128-wide K block's
+// fresh fp32 partial already carries it; the partial is then multiplied by the
+// block's weight scale (one value per tile: the tile spans one 128-column
+// weight block) and added to an fp64 master.  The tile's scale bytes are
+// staged in LDS, SEGB K blocks at a time.
+template <int NSLOT, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
+    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const uint8_t* __restrict__ ea,
+    const float* __restrict__ sbb, int tiles_m, int tiles_n) {
+  constexpr int BM = 128, BN = 128, TM = 2, TN = 2;  // 32-row subtiles per wavefront
+  constexpr int ROWS = BM + BN;
+  constexpr int SLOT = ROWS * kChunk;
+  constexpr int SEGS = SLOT / 1024;
+  constexpr int DPS = SEGS / 4;
+  constexpr int SEGB = 64;  // K blocks of activation scale bytes staged at a time
+  static_assert(NSLOT >= 2 && NSLOT <= 4, "ring depth");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSLOT * SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t esc[BM * SEGB / 4];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
+
+  const uint8_t* src[DPS];
+  int koff[DPS];
+#pragma unroll
+  for (int i = 0; i < DPS; ++i) {
+    const int seg = i * 4 + w;
+    const int row = seg * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz16(lane >> 2);
+    koff[i] = c * 16;
+    src[i] = row < BM ? A + (int64_t)min(m0 + row, M - 1) * lda + koff[i]
+                      : B + (int64_t)min(n0 + row - BM, N - 1) * ldb + koff[i];
+  }
+  const int nkc = (K + kChunk - 1) / kChunk;
+  const int nkb = (K + 127) / 128;
+  auto issue = [&](int kc) {
+    const uint32_t slot = lds0 + (uint32_t)((kc % NSLOT) * SLOT);
+    const int64_t kb = (int64_t)kc * kChunk;
+#pragma unroll
+    for (int i = 0; i < DPS; ++i) {
+      const void* p = kb + koff[i] < K ? (const void*)(src[i] + kb) : (const void*)g_zero16;
+      dma16(p, slot + (uint32_t)((i * 4 + w) * 1024));
+    }
+  };
+  // scale bytes of K blocks kb0 .. kb0 + SEGB - 1 for the tile's rows: thread t
+  // copies half a row (32 blocks); rows past M repeat row M - 1
+  auto stage_scales = [&](int kb0) {
+    const int row = t >> 1, half = t & 1;
+    const uint8_t* er = ea + (int64_t)min(m0 + row, M - 1) * nkb;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int kb = kb0 + half * 32 + 4 * q + b;
+        v |= (uint32_t)(kb < nkb ? er[kb] : 127) << (8 * b);
+      }
+      esc[(row * SEGB + half * 32 + 4 * q) / 4] = v;
+    }
+  };
+  const uint8_t* escb = reinterpret_cast<const uint8_t*>(esc);
+  const float* sbrow = sbb + (int64_t)tn * nkb;
+
+  const int a_off0 = wm * (BM / 2) * kChunk + frag32_off(lane, 0);
+  const int a_off1 = wm * (BM / 2) * kChunk + frag32_off(lane, 1);
+  const int b_off0 = (BM + wn * (BN / 2)) * kChunk + frag32_off(lane, 0);
+  const int b_off1 = (BM + wn * (BN / 2)) * kChunk + frag32_off(lane, 1);
+
+  f32x16 acc[TM][TN];
+  double mast[TM][TN][16];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc[i][j][v] = 0.f;
+        mast[i][j][v] = 0.0;
+      }
+  float asc[TM];
+  double sbk = 0.0;
+
+  for (int c = 0; c < NSLOT - 1 && c < nkc; ++c) issue(c);
+  stage_scales(0);  // visible after the first loop barrier
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int after = min(NSLOT - 2, nkc - 1 - kc);
+    if (after >= 2)
+      wait_vmcnt<2 * DPS>();
+    else if (after == 1)
+      wait_vmcnt<DPS>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // chunk kc visible to all; slot of chunk kc-1 free
+    const int kb = kc >> 1;
+    if ((kc & 1) == 0) {
+      if (kb > 0 && kb % SEGB == 0) {  // every wavefront is past the previous segment
+        stage_scales(kb);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        asc[i] = __uint_as_float((uint32_t)escb[(wm * 64 + 32 * i + (lane & 31)) * SEGB + kb % SEGB] << 23);
+      sbk = (double)sbrow[kb];
+    }
+    if (kc + NSLOT - 1 < nkc) issue(kc + NSLOT - 1);
+    const uint8_t* slot = lds + (kc % NSLOT) * SLOT;
+    Frag32 fa[TM], fb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      fa[i].q[0] = *reinterpret_cast<const uint4*>(slot + a_off0 + i * 32 * kChunk);
+      fa[i].q[1] = *reinterpret_cast<const uint4*>(slot + a_off1 + i * 32 * kChunk);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      fb[j].q[0] = *reinterpret_cast<const uint4*>(slot + b_off0 + j * 32 * kChunk);
+      fb[j].q[1] = *reinterpret_cast<const uint4*>(slot + b_off1 + j * 32 * kChunk);
+    }
+    mma32_chunk<TM, TN, true>(fa, asc, fb, acc);
+    if ((kc & 1) || kc == nkc - 1) {  // end of a K block: promote its partial
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            mast[i][j][v] = fma((double)acc[i][j][v], sbk, mast[i][j][v]);
+            acc[i][j][v] = 0.f;
+          }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = m0 + wm * (BM / 2) + 32 * i + (lane & 31);
+    if (r >= M) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = n0 + wn * (BN / 2) + 32 * j + 8 * v + 4 * (lane >> 5);
+        if (c >= N) continue;
+        const double* m4 = &mast[i][j][4 * v];
+        const uint32_t lo = (uint32_t)f64_to_bf16_rne(m4[0]) | ((uint32_t)f64_to_bf16_rne(m4[1]) << 16);
+        const uint32_t hi = (uint32_t)f64_to_bf16_rne(m4[2]) | ((uint32_t)f64_to_bf16_rne(m4[3]) << 16);
+        *reinterpret_cast<uint2*>(C + (int64_t)r * ldc + c) = make_uint2(lo, hi);
+      }
   }
 }
 
@@ -504,9 +743,10 @@ hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
 hipError_t launch_gemm_blockwise(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (int)((g.M + 127) / 128), tiles_n = (int)((g.N + 127) / 128);
   if (g.sa_kind == 3)
-    hipLaunchKernelGGL((gemm_blockwise_kernel<true>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
-                       g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, g.sa,
-                       static_cast<const float*>(g.sb), tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_block_ue8m0_kernel<4, 2>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
+                       g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
+                       static_cast<const uint8_t*>(g.sa), static_cast<const float*>(g.sb), tiles_m,
+                       tiles_n);
   else
     hipLaunchKernelGGL((gemm_blockwise_kernel<false>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
                        g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, g.sa,
