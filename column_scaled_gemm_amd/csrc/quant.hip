@@ -203,49 +203,159 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Per token, row kept in registers: one wavefront per row, NC 16-byte chunks
-// per lane (the host picks the smallest NC with 64 * NC * 8 >= K).
-template <bool F16, int NC, int FMT>
+// Per token, row kept in registers: persistent wavefronts walk the rows
+// (row, row + waves in the grid, ...), holding a row as NC 16-byte chunks per
+// lane (chunk c = lane + 64 i; the host picks the smallest listed NC with
+// 64 * NC * 8 >= K, so the last chunks of a lane may lie past the row end:
+// those read the row's last chunk and are masked out of the maximum and the
+// stores; chunks below NFULL, the next smaller listed NC, always lie inside
+// the row).  The next row's loads are issued before the current row is
+// reduced, quantized and stored, so every wave keeps one row in flight while
+// it writes the previous one.
+template <bool F16, int NC, int NFULL, int FMT>
 __global__ __launch_bounds__(256) void quant_token_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;  // whole wavefront; the kernel has no barrier
-  const int64_t nch = K >> 3;
-  const uint16_t* xr = x + row * ld_x;
-  uint4 v[NC];
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nch = (int)(K >> 3);  // K <= 2^30
+  int cidx[NC];
+  bool ok[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const int64_t c = lane + 64 * i;
-    v[i] = c < nch ? load_stream16(xr + c * 8)
-                   : make_uint4(0, 0, 0, 0);
+    const int c = lane + 64 * i;
+    ok[i] = i < NFULL || c < nch;
+    cidx[i] = i < NFULL ? c : min(c, nch - 1);
   }
-  float amax = 0.0f;
+  auto fetch = [&](uint4 (&v)[NC], int64_t r) {
+    const uint16_t* xr = x + r * ld_x;
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    float y[8];
-    widen8<F16>(v[i], y);
+    for (int i = 0; i < NC; ++i) v[i] = load_stream16(xr + (int64_t)cidx[i] * 8);
+  };
+  auto convert = [&](const uint4 (&v)[NC], int64_t r) {
+    // |x| max on the 16-bit patterns: with the sign cleared, bf16 and fp16
+    // values order like unsigned integers (inputs are finite)
+    u16x2 m2 = {0, 0};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(y[j]));
-  }
-  amax = group_max<64>(amax);
-  float sval;
-  int eb;
-  const float mult = group_multiplier<FMT>(amax, &sval, &eb);
-  uint8_t* qr = q + row * ld_q;
+    for (int i = 0; i < NC; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int64_t c = lane + 64 * i;
-    if (c < nch) {
+      for (int k = 0; k < 4; ++k)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, ok[i] ? (w[k] & 0x7FFF7FFFu) : 0u));
+    }
+    const uint32_t mb = m2[0] > m2[1] ? m2[0] : m2[1];
+    float amax;
+    if constexpr (F16)
+      amax = (float)__builtin_bit_cast(_Float16, (uint16_t)mb);
+    else
+      amax = __uint_as_float(mb << 16);
+    amax = group_max<64>(amax);
+    float sval;
+    int eb;
+    const float mult = group_multiplier<FMT>(amax, &sval, &eb);
+    uint8_t* qr = q + r * ld_q;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
       float y[8];
       widen8<F16>(v[i], y);
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
-      *reinterpret_cast<uint2*>(qr + c * 8) = to_e4m3_x8(y);
+      const uint2 codes = to_e4m3_x8(y);
+      if (ok[i]) *reinterpret_cast<uint2*>(qr + (int64_t)cidx[i] * 8) = codes;
     }
+    if (lane == 0) store_scale<FMT>(scales, r, sval, eb);
+  };
+  uint4 va[NC], vb[NC];
+  if (row < M) fetch(va, row);
+  while (row < M) {
+    const int64_t r1 = row + nw;
+    if (r1 < M) fetch(vb, r1);
+    convert(va, row);
+    row = r1;
+    if (row >= M) break;
+    const int64_t r2 = row + nw;
+    if (r2 < M) fetch(va, r2);
+    convert(vb, row);
+    row = r2;
   }
-  if (lane == 0) store_scale<FMT>(scales, row, sval, eb);
+}
+
+// Per token, long rows: the four wavefronts of a workgroup share a row, each
+// holding NCW 16-byte chunks per lane (chunk c = 64 w + lane + 256 i), with
+// the next row's quarter loaded while the current one is converted.  The row
+// maximum is exchanged through LDS (two slots, alternating by row, so one
+// barrier per row suffices); chunks past the row end are clamped and masked.
+template <bool F16, int NCW, int FMT>
+__global__ __launch_bounds__(256) void quant_token_wg_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
+  __shared__ float part[2][4];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nch = (int)(K >> 3);  // K <= 2^30
+  int cidx[NCW];
+  bool ok[NCW];
+#pragma unroll
+  for (int i = 0; i < NCW; ++i) {
+    const int c = 64 * w + lane + 256 * i;
+    ok[i] = c < nch;
+    cidx[i] = min(c, nch - 1);
+  }
+  auto fetch = [&](uint4 (&v)[NCW], int64_t r) {
+    const uint16_t* xr = x + r * ld_x;
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) v[i] = load_stream16(xr + (int64_t)cidx[i] * 8);
+  };
+  auto convert = [&](const uint4 (&v)[NCW], int64_t r, int par) {
+    u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) {
+      const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, ok[i] ? (wd[k] & 0x7FFF7FFFu) : 0u));
+    }
+    const uint32_t mb = m2[0] > m2[1] ? m2[0] : m2[1];
+    float amax;
+    if constexpr (F16)
+      amax = (float)__builtin_bit_cast(_Float16, (uint16_t)mb);
+    else
+      amax = __uint_as_float(mb << 16);
+    amax = group_max<64>(amax);
+    if (lane == 0) part[par][w] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[par][0], part[par][1]), fmaxf(part[par][2], part[par][3]));
+    float sval;
+    int eb;
+    const float mult = group_multiplier<FMT>(amax, &sval, &eb);
+    uint8_t* qr = q + r * ld_q;
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) {
+      float y[8];
+      widen8<F16>(v[i], y);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
+      const uint2 codes = to_e4m3_x8(y);
+      if (ok[i]) *reinterpret_cast<uint2*>(qr + (int64_t)cidx[i] * 8) = codes;
+    }
+    if (threadIdx.x == 0) store_scale<FMT>(scales, r, sval, eb);
+  };
+  uint4 va[NCW], vb[NCW];
+  int64_t row = blockIdx.x;
+  const int64_t stride = gridDim.x;
+  if (row < M) fetch(va, row);
+  while (row < M) {
+    const int64_t r1 = row + stride;
+    if (r1 < M) fetch(vb, r1);
+    convert(va, row, 0);
+    row = r1;
+    if (row >= M) break;
+    const int64_t r2 = row + stride;
+    if (r2 < M) fetch(va, r2);
+    convert(vb, row, 1);
+    row = r2;
+  }
 }
 
 // Per token, any K: two passes over the row (the second pass re-reads it from
@@ -464,12 +574,28 @@ static hipError_t launch_g128_fused(int fmt, const QuantArgs& a, hipStream_t s) 
   });
 }
 
-template <bool F16, int NC>
+// Resident 256-thread workgroups per CU for a kernel, queried once.
+template <typename Kern>
+static int resident_blocks(Kern k, std::atomic<int>& cache) {
+  int n = cache.load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 256, 0) != hipSuccess || n <= 0) n = 1;
+    cache.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// NC chunks per lane; the caller guarantees the row has more than 64 * NFULL
+// chunks (so chunks below NFULL are whole).
+template <bool F16, int NC, int NFULL>
 static hipError_t launch_token_nc(int fmt, const QuantArgs& a, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   return with_fmt(fmt, [&](auto f) {
     constexpr int FMT = decltype(f)::value;
-    hipLaunchKernelGGL((quant_token_kernel<F16, NC, FMT>), dim3((unsigned)((a.M + 3) / 4)),
+    static std::atomic<int> occ{0};
+    const int per_cu = resident_blocks(quant_token_kernel<F16, NC, NFULL, FMT>, occ);
+    const int64_t blocks = std::min<int64_t>((a.M + 3) / 4, (int64_t)per_cu * cu_count());
+    hipLaunchKernelGGL((quant_token_kernel<F16, NC, NFULL, FMT>), dim3((unsigned)blocks),
                        dim3(256), 0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
   });
 }
@@ -495,17 +621,34 @@ static hipError_t launch_token_fused(int fmt, const QuantArgs& a, hipStream_t s)
   });
 }
 
+template <bool F16, int NCW>
+static hipError_t launch_token_wg(int fmt, const QuantArgs& a, hipStream_t s) {
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  return with_fmt(fmt, [&](auto f) {
+    constexpr int FMT = decltype(f)::value;
+    static std::atomic<int> occ{0};
+    const int per_cu = resident_blocks(quant_token_wg_kernel<F16, NCW, FMT>, occ);
+    const int64_t blocks = std::min<int64_t>(a.M, (int64_t)per_cu * cu_count());
+    hipLaunchKernelGGL((quant_token_wg_kernel<F16, NCW, FMT>), dim3((unsigned)blocks), dim3(256),
+                       0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+  });
+}
+
 template <bool F16>
 static hipError_t launch_token(int fmt, const QuantArgs& a, hipStream_t s) {
   const int64_t per_lane = (a.K / 8 + 63) / 64;
-  if (per_lane <= 1) return launch_token_nc<F16, 1>(fmt, a, s);
-  if (per_lane <= 2) return launch_token_nc<F16, 2>(fmt, a, s);
-  if (per_lane <= 4) return launch_token_nc<F16, 4>(fmt, a, s);
-  if (per_lane <= 8) return launch_token_nc<F16, 8>(fmt, a, s);
-  if (per_lane <= 12) return launch_token_nc<F16, 12>(fmt, a, s);
-  if (per_lane <= 16) return launch_token_nc<F16, 16>(fmt, a, s);
-  if (per_lane <= 24) return launch_token_nc<F16, 24>(fmt, a, s);
-  if (per_lane <= 32) return launch_token_nc<F16, 32>(fmt, a, s);
+  if (per_lane <= 1) return launch_token_nc<F16, 1, 0>(fmt, a, s);
+  if (per_lane <= 2) return launch_token_nc<F16, 2, 1>(fmt, a, s);
+  if (per_lane <= 4) return launch_token_nc<F16, 4, 2>(fmt, a, s);
+  if (per_lane <= 6) return launch_token_nc<F16, 6, 4>(fmt, a, s);
+  if (per_lane <= 8) return launch_token_nc<F16, 8, 6>(fmt, a, s);
+  if (per_lane <= 11) return launch_token_nc<F16, 11, 8>(fmt, a, s);
+  if (per_lane <= 14) return launch_token_nc<F16, 14, 11>(fmt, a, s);
+  const int64_t per_wave = (a.K / 8 + 255) / 256;  // chunks per lane with 4 waves per row
+  if (per_wave <= 4) return launch_token_wg<F16, 4>(fmt, a, s);
+  if (per_wave <= 6) return launch_token_wg<F16, 6>(fmt, a, s);
+  if (per_wave <= 8) return launch_token_wg<F16, 8>(fmt, a, s);
+  if (per_wave <= 12) return launch_token_wg<F16, 12>(fmt, a, s);
   return launch_token_2pass<F16>(fmt, a, s);
 }
 

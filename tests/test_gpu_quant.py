@@ -67,11 +67,23 @@ def test_group128_all_formats(dtype, fmt, layout):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("K", [8, 64, 384, 4224, 5376, 14336, 20480])
+@pytest.mark.parametrize("K", [8, 64, 384, 1008, 2000, 3056, 4096, 4224, 5376, 7168, 7184, 12288,
+                               14336, 16384, 20480, 24592])
 def test_per_token_fp32_many_widths(dtype, K):
-    # widths cover every register-resident variant and the two-pass kernel
+    # widths cover every row-in-registers variant (one wavefront per row: 1, 2,
+    # 4, 6, 8, 11 and 14 chunks per lane; four wavefronts per row: 4, 6, 8 and
+    # 12 chunks per lane), each with a partial last chunk where K allows, and
+    # the two-pass kernel
     x = _mixed_rows(9, K, dtype, seed=2)
     _check(x, -1, 0, 0, what="per-token")
+
+
+@pytest.mark.parametrize("M,K", [(2600, 14336), (5000, 1024)])
+def test_per_token_many_rows(M, K):
+    # more rows than resident wavefronts / workgroups: every wavefront walks
+    # several rows, alternating its two row buffers
+    x = _mixed_rows(M, K, torch.bfloat16, seed=7)
+    _check(x, -1, 0, 0, what="per-token many rows")
 
 
 @pytest.mark.parametrize("fmt", [1, 2])
