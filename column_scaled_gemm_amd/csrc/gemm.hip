@@ -497,7 +497,12 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 // Decode kernel (M <= 16 * TM): one wavefront owns 16 output columns and walks
 // all of K in the canonical order, streaming A and B straight into registers
 // D chunks ahead (software pipelined: chunk c + D is requested while chunk c
-// is multiplied).
+// is multiplied).  The nf = K / 64 whole chunks are loaded branch-free from a
+// wave-uniform base plus a 32-bit lane offset (requests past chunk nf - 1
+// re-read it and are never used), so the compiler's wait counts keep the D
+// chunks in flight.  A partial last chunk is loaded on its own: a lane's 16
+// bytes past K are read from the row's last 16 bytes, and its A values there
+// are zeroed before the multiply (B's duplicates then meet zeros).
 template <int TM, int D>
 __global__ __launch_bounds__(64) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
@@ -506,40 +511,63 @@ __global__ __launch_bounds__(64) void gemm_decode_kernel(
   const int lane = threadIdx.x;
   const int g = lane >> 4, r16 = lane & 15;
   const int n0 = blockIdx.x * 16;
-  const int nkc = (K + kChunk - 1) / kChunk;
-  const uint8_t* brow = B + (int64_t)min(n0 + r16, N - 1) * ldb + 16 * g;
-  const uint8_t* arow[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) arow[i] = A + (int64_t)min(16 * i + r16, M - 1) * lda + 16 * g;
+  const int nf = K / kChunk;  // whole chunks
   const int kl = 16 * g;
-  auto ld = [&](const uint8_t* p, int kc) -> uint4 {
-    const int64_t k0 = (int64_t)kc * kChunk;
-    return k0 + kl < K ? *reinterpret_cast<const uint4*>(p + k0) : make_uint4(0, 0, 0, 0);
+  // byte offsets within a 16-row panel (rows past N / M repeat the last row);
+  // 16 * max(lda, ldb) stays far below 2^32 for K <= 65536 and 16-byte rows
+  const uint32_t bo = (uint32_t)(min(r16, N - 1 - n0) * ldb + kl);
+  const uint8_t* bbase = B + (int64_t)n0 * ldb;
+  uint32_t ao[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) ao[i] = (uint32_t)(min(16 * i + r16, M - 1) * lda + kl);
+  auto ldb16 = [&](int kc) -> uint4 {
+    return *reinterpret_cast<const uint4*>(bbase + (int64_t)kc * kChunk + bo);
+  };
+  auto lda16 = [&](int i, int kc) -> uint4 {
+    return *reinterpret_cast<const uint4*>(A + (int64_t)kc * kChunk + ao[i]);
   };
   f32x4 acc[TM][1];
 #pragma unroll
   for (int i = 0; i < TM; ++i) acc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint4 rb[D], ra[D][TM];
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    rb[d] = ld(brow, d);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) ra[d][i] = ld(arow[i], d);
-  }
-  for (int kc0 = 0; kc0 < nkc; kc0 += D) {
+  auto mma = [&](const uint4& fbv, const uint4 (&fa)[TM]) {
+    const uint4 fb[1] = {fbv};
+    mma_chunk64<TM, 1>(fa, fb, acc);
+  };
+  if (nf > 0) {
+    uint4 rb[D], ra[D][TM];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (kc0 + d < nkc) {
-        uint4 fb[1] = {rb[d]};
-        uint4 fa[TM];
+      const int kc = min(d, nf - 1);
+      rb[d] = ldb16(kc);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[i] = ra[d][i];
-        mma_chunk64<TM, 1>(fa, fb, acc);
-      }
-      rb[d] = ld(brow, kc0 + d + D);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) ra[d][i] = ld(arow[i], kc0 + d + D);
+      for (int i = 0; i < TM; ++i) ra[d][i] = lda16(i, kc);
     }
+    int kc0 = 0;
+    for (; kc0 + D <= nf; kc0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        mma(rb[d], ra[d]);
+        const int kc = min(kc0 + d + D, nf - 1);
+        rb[d] = ldb16(kc);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) ra[d][i] = lda16(i, kc);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (kc0 + d < nf) mma(rb[d], ra[d]);
+  }
+  if (nf * kChunk < K) {  // partial last chunk
+    const bool in = nf * kChunk + kl < K;
+    const int64_t shift = in ? 0 : (int64_t)(K - 16) - (nf * kChunk + kl);  // to the row's last 16 bytes
+    const uint4 fb = *reinterpret_cast<const uint4*>(bbase + (int64_t)nf * kChunk + bo + shift);
+    uint4 fa[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(A + (int64_t)nf * kChunk + ao[i] + shift);
+      fa[i] = in ? v : make_uint4(0, 0, 0, 0);
+    }
+    mma(fb, fa);
   }
   const int c = n0 + r16;
   if (c >= N) return;
@@ -733,7 +761,7 @@ hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
     case VAR_TILE_256x128: return launch_rowwise_tile<256, 128, 3, 2>(g, s);
     case VAR_TILE_128x128: return launch_rowwise_tile<128, 128, 4, 2>(g, s);
     case VAR_TILE_128x256: return launch_rowwise_tile<128, 256, 3, 2>(g, s);
-    case VAR_DECODE_16: return launch_decode<1, 16>(g, s);
+    case VAR_DECODE_16: return launch_decode<1, 24>(g, s);
     case VAR_DECODE_32: return launch_decode<2, 12>(g, s);
     case VAR_DECODE_64: return launch_decode<4, 8>(g, s);
     default: return hipErrorInvalidValue;
