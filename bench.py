@@ -33,8 +33,8 @@ PEAK_HBM = 8000.0           # GB/s
 # passes, scaled by a plain-copy calibration (profiles/
 # gemm_rowwise_128x256_qkv_traffic.md).  Valid only for the gemm.hip source it
 # was measured on; reported as null once that file changes.
-TRAFFIC = {"gemm_src_sha256_prefix": "8dda0789fda686bc", "workload": "qkv",
-           "kernel": "tile128x256", "bytes": 2208e6 + 584.4e6}
+TRAFFIC = {"gemm_src_sha256_prefix": "1d3ddf8fb09c4bef", "workload": "qkv",
+           "kernel": "tile128x256", "bytes": 2187.2e6 + 358.2e6}
 
 
 def measured_traffic(workload, variant):
@@ -51,7 +51,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=15,
+                   help="untimed steps; the GEMM settles over its first ~10 back-to-back launches")
     p.add_argument("--workload", default="qkv",
                    choices=["qkv", "mlp_gateup_23216", "mlp_gateup_15760", "mlp_down", "tiny"])
     p.add_argument("--variant", default=None,
