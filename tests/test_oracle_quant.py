@@ -311,3 +311,90 @@ def test_weight_block_quant_matches_row_quant_on_single_row_blocks():
     assert np.array_equal(codes[0], r.codes[0])
     assert np.array_equal(scales[0], r.scale[0])
     assert scales.shape == (1, 2)
+
+
+# ------------------------------------------------------- 128 x 128 weight blocks
+# Pins of the offline weight block quant that do not reuse its arithmetic:
+# the hardware-independent torch cast where the multiplier is a power of two,
+# the zero-block closed form, and invariants that catch a wrong block index,
+# a transposed block or an edge block taking elements from outside itself.
+
+def _blocks_with_power_of_two_maxima(nb, kb, js, rng, sign_flip=False):
+    """[128 nb, 128 kb] array whose block (i, j) holds values in (-448, 448)
+    times 2^js[i][j] with one element exactly +-448 * 2^js[i][j]."""
+    w = np.clip(rng.standard_normal((128 * nb, 128 * kb)) * 80, -447, 447).astype(F32)
+    base = w.copy()
+    for i in range(nb):
+        for j in range(kb):
+            r, c = 128 * i + (7 * i + 3 * j) % 128, 128 * j + (11 * j + 5 * i) % 128
+            base[r, c] = F32(-448.0 if (sign_flip and (i + j) % 2) else 448.0)
+            w[128 * i:128 * (i + 1), 128 * j:128 * (j + 1)] = \
+                base[128 * i:128 * (i + 1), 128 * j:128 * (j + 1)] * F32(2.0 ** js[i][j])
+    return w.astype(F32), base
+
+
+def test_weight_block_unit_maximum_gives_torch_codes():
+    rng = np.random.Generator(np.random.PCG64(40))
+    w, base = _blocks_with_power_of_two_maxima(2, 3, [[0] * 3] * 2, rng, sign_flip=True)
+    codes, scales = quant.quant_weight_block(w)
+    assert np.all(scales == F32(1.0))
+    assert np.array_equal(codes, _torch_encode(base))
+
+
+def test_weight_block_power_of_two_maxima_give_exact_scales_per_block():
+    # a different power of two in every block: a transposed or shifted block
+    # index lands a wrong scale or wrongly scaled codes somewhere
+    rng = np.random.Generator(np.random.PCG64(41))
+    js = [[-9, 3, 0], [12, -20, 5]]
+    w, base = _blocks_with_power_of_two_maxima(2, 3, js, rng)
+    codes, scales = quant.quant_weight_block(w)
+    assert np.array_equal(scales, np.array([[2.0 ** j for j in row] for row in js], F32))
+    assert np.array_equal(codes, _torch_encode(base))
+
+
+def test_weight_block_zero_block_closed_form():
+    g = _golden()
+    rng = np.random.Generator(np.random.PCG64(42))
+    w = rng.standard_normal((256, 256)).astype(F32)
+    w[128:, :128] = 0
+    codes, scales = quant.quant_weight_block(w)
+    assert scales[1, 0] == F32(float(g["zero_group_scale_f32"]))
+    assert np.all(codes[128:, :128] == int(g["zero_group_code"], 16))
+
+
+def test_weight_block_edges_equal_zero_padded_full_blocks():
+    # a partial edge block takes its maximum from its own elements only: the
+    # same values zero-padded to whole blocks (zeros never raise a maximum)
+    # give the same scales and codes
+    rng = np.random.Generator(np.random.PCG64(43))
+    w = (rng.standard_normal((130, 200)) * 0.02).astype(F32)
+    w[129, 150] = F32(5.0)                 # the largest value sits in edge block (1, 1)
+    codes, scales = quant.quant_weight_block(w)
+    pad = np.zeros((256, 256), F32)
+    pad[:130, :200] = w
+    cp, sp = quant.quant_weight_block(pad)
+    assert scales.shape == (2, 2)
+    assert np.array_equal(scales, sp)
+    assert np.array_equal(codes, cp[:130, :200])
+    assert scales[1, 1] > 20 * scales[0, 0]  # the planted maximum sets the edge block
+
+
+def test_weight_block_blocks_are_independent_and_sign_symmetric():
+    rng = np.random.Generator(np.random.PCG64(44))
+    w = (rng.standard_normal((256, 384)) * 0.02).astype(F32)
+    codes, scales = quant.quant_weight_block(w)
+    y = w.copy()
+    y[128:, 128:256] *= F32(1000.0)        # only block (1, 1) changes
+    c2, s2 = quant.quant_weight_block(y)
+    mask = np.ones((256, 384), bool)
+    mask[128:, 128:256] = False
+    assert np.array_equal(codes[mask], c2[mask])
+    keep = np.ones((2, 3), bool)
+    keep[1, 1] = False
+    assert np.array_equal(scales[keep], s2[keep]) and s2[1, 1] != scales[1, 1]
+    cn, sn = quant.quant_weight_block(-w)
+    assert np.array_equal(sn, scales) and np.array_equal(cn, codes ^ 0x80)
+    for j in (-12, 7):
+        cj, sj = quant.quant_weight_block((w * F32(2.0 ** j)).astype(F32))
+        assert np.array_equal(cj, codes)
+        assert np.array_equal(sj, (scales * F32(2.0 ** j)).astype(F32))
