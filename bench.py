@@ -96,9 +96,12 @@ def cpu_baseline(w, M, N, K, target_s):
         return time.perf_counter() - t0
 
     R = 16
-    t = run(R)
-    R = int(max(16, min(M, R * target_s / max(t, 1e-3))))
-    t = run(R)
+    t = run(R)                       # also warms up the BLAS threads
+    for _ in range(4):               # rescale until the sample is near the target
+        R = int(max(16, min(M, R * target_s / max(t, 1e-3))))
+        t = run(R)
+        if t >= 0.5 * target_s or R == M:
+            break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(2.0 * R * N * K / t / 1e12, 6), "unit": "TFLOP/s",
             "cores": int(threads), "kind": "oracle",
