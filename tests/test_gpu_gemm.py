@@ -82,7 +82,12 @@ def _quantized_case(M, N, K, seed, outliers=True):
 
 
 @pytest.mark.parametrize("shape", [(1, 8, 16), (37, 264, 80), (100, 136, 208), (130, 520, 1040),
-                                   (64, 256, 512), (257, 128, 4096), (33, 1000, 2064)])
+                                   (64, 256, 512), (257, 128, 4096), (33, 1000, 2064),
+                                   # K % 64 = 48 / 32 / 48, and K around the decode
+                                   # kernels' prefetch depths (24 chunks for M <= 32,
+                                   # 8 for M <= 64): below, exactly at, just past
+                                   (5, 24, 48), (16, 40, 96), (3, 64, 176), (16, 48, 1472),
+                                   (16, 48, 1536), (16, 48, 1552), (64, 72, 1552)])
 def test_ragged_shapes_every_variant_bitwise_equal_and_within_bound(shape):
     M, N, K = shape
     print(f"[case] ragged M={M} N={N} K={K}", flush=True)
@@ -95,6 +100,31 @@ def test_ragged_shapes_every_variant_bitwise_equal_and_within_bound(shape):
     first = next(iter(outs.values()))
     for v, o in outs.items():
         assert np.array_equal(o, first), f"variant {fp8sm.variant_name(v)} differs bitwise"
+
+
+def test_padded_leading_dimensions():
+    # A, B and C as views into wider buffers: results equal the compact call
+    # bitwise in every variant, and C's padding columns are left untouched
+    M, N, K = 40, 72, 336
+    A, B, sa, sb = _quantized_case(M, N, K, seed=91)
+    Ab = torch.zeros((M, K + 32), dtype=torch.uint8)
+    Bb = torch.zeros((N, K + 48), dtype=torch.uint8)
+    Ab[:, :K] = torch.from_numpy(A)
+    Bb[:, :K] = torch.from_numpy(B)
+    Ag, Bg = Ab.to(cuda())[:, :K], Bb.to(cuda())[:, :K]
+    sag, sbg = to_gpu_f32(sa), to_gpu_f32(sb)
+    for v in _variants_for(M):
+        prev = fp8sm.force_variant(v)
+        try:
+            Cb = torch.full((M, N + 8), 3.0, dtype=torch.bfloat16, device=cuda())
+            fp8sm.scaled_mm(Ag, Bg, sag, sbg, fp8sm.KIND_ROW, fp8sm.KIND_COL, c=Cb[:, :N])
+            ref = fp8sm.scaled_mm(to_gpu_u8(A), to_gpu_u8(B), sag, sbg, fp8sm.KIND_ROW,
+                                  fp8sm.KIND_COL)
+            torch.cuda.synchronize()
+        finally:
+            fp8sm.force_variant(prev)
+        assert np.array_equal(bf16_bits(Cb[:, :N].contiguous()), bf16_bits(ref)), fp8sm.variant_name(v)
+        assert torch.all(Cb[:, N:] == 3.0), fp8sm.variant_name(v)
 
 
 def test_rows_do_not_depend_on_m():
