@@ -69,10 +69,26 @@ __device__ __forceinline__ float pow2f(int e) {  // 2^e, -126 <= e <= 127
   return __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
+// v from lane (l + N) mod 16 of the same 16-lane DPP row.
+template <int N>
+__device__ __forceinline__ float dpp_row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Maximum over aligned groups of WIDTH lanes (16 or 64), returned in every
+// lane of the group.  Within a 16-lane row: four DPP rotations; across the
+// rows of a wavefront: two lane shuffles.
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int off = WIDTH / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  static_assert(WIDTH == 16 || WIDTH == 64, "group width");
+  v = fmaxf(v, dpp_row_ror<8>(v));
+  v = fmaxf(v, dpp_row_ror<4>(v));
+  v = fmaxf(v, dpp_row_ror<2>(v));
+  v = fmaxf(v, dpp_row_ror<1>(v));
+  if constexpr (WIDTH == 64) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+  }
   return v;
 }
 

@@ -59,8 +59,18 @@ __device__ __forceinline__ void load_values(const uint4 gv, const uint4 uv, floa
   if constexpr (FUSED) {
     float u[8];
     widen8<F16>(uv, u);
+    if constexpr (F16) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = SiluTable<F16>::lookup(tab, y[i]) * u[i];
+      for (int i = 0; i < 8; ++i) y[i] = SiluTable<true>::lookup(tab, y[i]) * u[i];
+    } else {
+      // bf16 gates: index the table from the raw 16-bit halves
+      const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[2 * i] = SiluTable<false>::lookup_bits(tab, y[2 * i], w[i] & 0x7FFFu, (w[i] >> 15) & 1u) * u[2 * i];
+        y[2 * i + 1] = SiluTable<false>::lookup_bits(tab, y[2 * i + 1], (w[i] >> 16) & 0x7FFFu, w[i] >> 31) * u[2 * i + 1];
+      }
+    }
   }
 }
 
@@ -86,6 +96,27 @@ __device__ __forceinline__ void quant_group128(float* y, int l16, int64_t row, i
       const int64_t idx = mn_major ? grp * mpad + row : row * G + grp;
       store_scale<FMT>(scales, idx, sval, eb);
     }
+  }
+}
+
+// The same group conversion with 32-bit byte offsets: qo is the group's first
+// code offset in q plus l16 * 8, so = its scale index.
+template <int FMT>
+__device__ __forceinline__ void quant_group128_o32(float* y, int l16, bool valid,
+                                                   uint8_t* __restrict__ q, uint32_t qo,
+                                                   void* __restrict__ scales, uint32_t so) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
+  amax = group_max<16>(amax);
+  float sval;
+  int eb;
+  const float mult = group_multiplier<FMT>(amax, &sval, &eb);
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = y[i] * mult;
+    *reinterpret_cast<uint2*>(q + qo) = to_e4m3_x8(y);
+    if (l16 == 0) store_scale<FMT>(scales, so, sval, eb);
   }
 }
 
@@ -141,7 +172,7 @@ struct G128Step {
   int row[kQuads], grp[kQuads];  // row = -1: past the end
 };
 
-template <bool F16, int FMT>
+template <bool F16, int FMT, bool O32>
 __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
     const uint16_t* __restrict__ x, int M, int G, int64_t K, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, int mn_major,
@@ -163,13 +194,20 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
     cr[u] = (int)(gid / G);
     cc[u] = (int)(gid - (int64_t)cr[u] * G);
   }
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
   auto fetch = [&](G128Step& st) {
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
       const int r = min(cr[u], M - 1);
-      const uint16_t* src = x + (int64_t)r * ld_x + (int64_t)cc[u] * 128 + l16 * 8;
-      st.g[u] = load_stream16(src);
-      st.u[u] = load_stream16(src + K);
+      if constexpr (O32) {
+        const uint32_t off = (uint32_t)r * (uint32_t)(2 * ld_x) + (uint32_t)cc[u] * 256u + l16 * 16u;
+        st.g[u] = load_stream16(xb + off);
+        st.u[u] = load_stream16(xb + (off + (uint32_t)(2 * K)));
+      } else {
+        const uint16_t* src = x + (int64_t)r * ld_x + (int64_t)cc[u] * 128 + l16 * 8;
+        st.g[u] = load_stream16(src);
+        st.u[u] = load_stream16(src + K);
+      }
       st.row[u] = cr[u] < M ? cr[u] : -1;
       st.grp[u] = cc[u];
       // advance the cursor to the wavefront's next step
@@ -184,7 +222,14 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
     for (int u = 0; u < kQuads; ++u) {
       float y[8];
       load_values<F16, true>(st.g[u], st.u[u], y, tab);
-      quant_group128<FMT>(y, l16, st.row[u], st.grp[u], q, ld_q, scales, G, mn_major, mpad);
+      if constexpr (O32) {
+        const uint32_t rr = (uint32_t)max(st.row[u], 0), gg = (uint32_t)st.grp[u];
+        const uint32_t qo = rr * (uint32_t)ld_q + gg * 128u + l16 * 8u;
+        const uint32_t so = mn_major ? gg * (uint32_t)mpad + rr : rr * (uint32_t)G + gg;
+        quant_group128_o32<FMT>(y, l16, st.row[u] >= 0, q, qo, scales, so);
+      } else {
+        quant_group128<FMT>(y, l16, st.row[u], st.grp[u], q, ld_q, scales, G, mn_major, mpad);
+      }
     }
   };
   G128Step a, b;
@@ -567,10 +612,21 @@ static hipError_t launch_g128_fused(int fmt, const QuantArgs& a, hipStream_t s) 
   const int64_t G = a.K / 128;
   const unsigned blocks = persistent_blocks(16 * 16, a.M * G);  // 16 waves x 16 groups
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  // every byte offset the kernel forms below 2^32: 32-bit address arithmetic
+  const uint64_t lim = (uint64_t)1 << 32;
+  const bool o32 = (uint64_t)a.M * (uint64_t)a.ld_x * 2 + 2 * (uint64_t)a.K < lim &&
+                   (uint64_t)a.M * (uint64_t)a.ld_q < lim &&
+                   (uint64_t)(a.mn_major ? G * a.mpad : a.M * G) < lim;
   return with_fmt(fmt, [&](auto f) {
     constexpr int FMT = decltype(f)::value;
-    hipLaunchKernelGGL((quant_g128_fused_kernel<F16, FMT>), dim3(blocks), dim3(1024), 0, s, x,
-                       (int)a.M, (int)G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad);
+    if (o32)
+      hipLaunchKernelGGL((quant_g128_fused_kernel<F16, FMT, true>), dim3(blocks), dim3(1024), 0,
+                         s, x, (int)a.M, (int)G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major,
+                         a.mpad);
+    else
+      hipLaunchKernelGGL((quant_g128_fused_kernel<F16, FMT, false>), dim3(blocks), dim3(1024), 0,
+                         s, x, (int)a.M, (int)G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major,
+                         a.mpad);
   });
 }
 

@@ -59,8 +59,17 @@ struct SiluTable<false> {
 
   __device__ static float lookup(const void* lds, float g) {
     const uint32_t b = __float_as_uint(g);
-    const uint32_t e = min(max((b >> 23) & 255u, kE0), kE0 + kRows - 1) - kE0;
-    const uint32_t idx = (((b >> 31) * kRows + e) << 7) | ((b >> 16) & 127u);
+    return lookup_bits(lds, g, (b >> 16) & 0x7FFFu, b >> 31);
+  }
+
+  // The same from the gate's bf16 pattern: mag = its low 15 bits, s = its
+  // sign bit.  Clamping mag (positive bf16 patterns order like integers) to
+  // [E=100 m=0, E=134 m=127] selects the row and mantissa in one step; the
+  // table is [sign][row][mantissa], so the entry is s * 4480 + mag - 12800.
+  __device__ static float lookup_bits(const void* lds, float g, uint32_t mag, uint32_t s) {
+    const uint32_t lo = kE0 << 7, hi = ((kE0 + kRows - 1) << 7) | 127u;
+    const uint32_t mc = min(max(mag, lo), hi);
+    const uint32_t idx = s * (kRows * 128) + mc - lo;
     const float2 ab = static_cast<const float2*>(lds)[idx];
     return __builtin_fmaf(g, ab.x, ab.y);
   }
