@@ -10,6 +10,17 @@ PR #33148, key source excerpts):
     acc[m, n] = sum_k dec(A[m, k]) * dec(B[n, k])          (exact)
     out[m, n] = bf16( acc[m, n] * (sa[m] * sb[n]) )
 
+With the optional epilogue of the deterministic FP8 linear (sglang PR #44861,
+Modifications: tests with bias and BF16/FP16 outputs; the linear's apply()
+passes an optional bias, prhub digest of PR #33148, key source excerpts):
+
+    out[m, n] = rnd( acc[m, n] * (sa[m] * sb[n]) + bias[n] )
+
+with bias a vector of output-dtype values and rnd the round-to-nearest-even
+conversion to bf16 or fp16 (fp16 overflows to +-inf) -- the pages print no
+order of the epilogue operations; this is the plain reading, computed in
+float64 and rounded once.
+
 A is [M, K] row-major, B is [N, K] with K contiguous (the [K, N]
 column-major weight of the digest's excerpt), sa/sb are fp32 vectors or
 scalars.
@@ -43,6 +54,7 @@ import numpy as np
 
 from . import e4m3
 from .bf16 import to_bf16_bits, bits_to_f64
+from . import fp16 as _fp16
 
 KMAX_EXACT = 1 << 17
 
@@ -57,18 +69,20 @@ def _as_vec(s, n):
 
 
 class MMResult:
-    """bits: bf16 output [M, N] as uint16; value: float64 before the bf16
-    rounding; acc: exact accumulator; sab: sa[m] * sb[n] (exact)."""
+    """bits: output [M, N] as uint16 (bf16, or fp16 when out == "fp16");
+    value: float64 before the output rounding; acc: exact accumulator;
+    sab: sa[m] * sb[n] (exact)."""
 
-    def __init__(self, bits, value, acc, sab):
+    def __init__(self, bits, value, acc, sab, out="bf16"):
         self.bits = bits
         self.value = value
         self.acc = acc
         self.sab = sab
+        self.dtype = out
 
     @property
     def out(self):
-        return bits_to_f64(self.bits)
+        return _fp16.bits_to_f64(self.bits) if self.dtype == "fp16" else bits_to_f64(self.bits)
 
 
 def accumulate(a_codes, b_codes, chunk=4096):
@@ -97,8 +111,9 @@ def accumulate(a_codes, b_codes, chunk=4096):
     return acc
 
 
-def scaled_mm(a_codes, b_codes, sa, sb):
-    """Rowwise (sa [M], sb [N]) or per-tensor (scalars) scaled GEMM."""
+def scaled_mm(a_codes, b_codes, sa, sb, bias=None, out="bf16"):
+    """Rowwise (sa [M], sb [N]) or per-tensor (scalars) scaled GEMM; bias:
+    None or [N] output-dtype values (as floats); out: "bf16" or "fp16"."""
     M = np.asarray(a_codes).shape[0]
     N = np.asarray(b_codes).shape[0]
     acc = accumulate(a_codes, b_codes)
@@ -106,6 +121,12 @@ def scaled_mm(a_codes, b_codes, sa, sb):
     sb64 = _as_vec(sb, N).astype(np.float64)
     sab = sa64[:, None] * sb64[None, :]
     value = acc * sab
+    if bias is not None:
+        value = value + np.asarray(bias, dtype=np.float64).reshape(1, N)
+    if out == "fp16":
+        return MMResult(_fp16.to_fp16_bits(value), value, acc, sab, out)
+    if out != "bf16":
+        raise ValueError("out must be 'bf16' or 'fp16'")
     return MMResult(to_bf16_bits(value), value, acc, sab)
 
 
@@ -136,7 +157,7 @@ def blockwise_mm(a_codes, a_scale, b_codes, b_scale, block=128):
     return MMResult(to_bf16_bits(total), total, None, smax)
 
 
-def scaled_mm_entries(a_codes, b_codes, sa, sb, rows, cols):
+def scaled_mm_entries(a_codes, b_codes, sa, sb, rows, cols, bias=None, out="bf16"):
     """The rowwise GEMM on the sub-grid rows x cols only (for sampled checks
     at full size).  Same definition as scaled_mm."""
     a_codes = np.asarray(a_codes, dtype=np.uint8)
@@ -147,4 +168,5 @@ def scaled_mm_entries(a_codes, b_codes, sa, sb, rows, cols):
     N = b_codes.shape[0]
     sa_v = _as_vec(sa, M)[rows]
     sb_v = _as_vec(sb, N)[cols]
-    return scaled_mm(a_codes[rows], b_codes[cols], sa_v, sb_v)
+    b_v = None if bias is None else np.asarray(bias).reshape(-1)[cols]
+    return scaled_mm(a_codes[rows], b_codes[cols], sa_v, sb_v, b_v, out)

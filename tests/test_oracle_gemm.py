@@ -208,3 +208,57 @@ def test_rowwise_pipeline_from_bf16_inputs():
     r = gemm.scaled_mm(qa.codes, qb.codes, qa.scale.reshape(-1), qb.scale.reshape(-1))
     want = x.astype(np.float64) @ w.T.astype(np.float64)
     assert np.array_equal(r.out, bf16.round_to_bf16(want))
+
+
+# ------------------------------------------------------------- bias / fp16 out
+
+def test_bias_and_fp16_output_integer_closed_forms():
+    # sums of +-1 * 2 products are small integers: acc * sa * sb + bias is an
+    # exact small integer in both output dtypes
+    one = e4m3.encode(np.float32([1.0]))[0]
+    two = e4m3.encode(np.float32([2.0]))[0]
+    K = 100
+    A = np.full((2, K), one, np.uint8)
+    A[1, :60] = one | 0x80                                # row 1: (40 - 60) * 2 = -40
+    B = np.full((3, K), two, np.uint8)
+    bias = np.array([3.0, -5.0, 0.5])
+    # 200.5 needs 9 significant bits: a bf16 tie between 200 and 201 -> 200;
+    # fp16 (11 bits) holds it
+    want = {"bf16": [[203.0, 195.0, 200.0], [-37.0, -45.0, -39.5]],
+            "fp16": [[203.0, 195.0, 200.5], [-37.0, -45.0, -39.5]]}
+    for out in ("bf16", "fp16"):
+        r = gemm.scaled_mm(A, B, 1.0, 1.0, bias=bias, out=out)
+        assert r.dtype == out
+        assert np.array_equal(r.out, np.array(want[out]))
+
+
+def test_fp16_output_overflows_to_inf():
+    big = e4m3.encode(np.float32([448.0]))[0]
+    A = np.full((1, 16), big, np.uint8)
+    B = np.full((2, 16), big, np.uint8)                   # 16 * 448^2 = 3.2e6
+    r = gemm.scaled_mm(A, B, 1.0, np.float32([1.0, 2.0 ** -7]), out="fp16")
+    assert np.isinf(r.out[0, 0]) and r.out[0, 0] > 0
+    assert r.out[0, 1] == 25088.0                          # 3211264 / 128, exact in fp16
+
+
+def test_zero_bias_is_no_bias_and_matches_torch_casts():
+    rng = np.random.Generator(np.random.PCG64(61))
+    A = _rand_codes(rng, (7, 96))
+    B = _rand_codes(rng, (9, 96))
+    sa = (rng.random(7) * 1e-2).astype(F32)
+    sb = (rng.random(9) * 1e-2).astype(F32)
+    base = gemm.scaled_mm(A, B, sa, sb)
+    z = gemm.scaled_mm(A, B, sa, sb, bias=np.zeros(9))
+    assert np.array_equal(base.bits, z.bits)
+    # torch: float64 matmul of the decoded codes, scaled, plus bias, then the
+    # library's float64 -> bf16 / fp16 conversions (via float32, where a double
+    # rounding can differ: compare within one unit of the last place)
+    bias = rng.standard_normal(9) * 4
+    ta = torch.from_numpy(e4m3.decode(A))
+    tb = torch.from_numpy(e4m3.decode(B))
+    v = (ta @ tb.T) * torch.from_numpy(sa.astype(np.float64))[:, None] \
+        * torch.from_numpy(sb.astype(np.float64))[None, :] + torch.from_numpy(bias)[None, :]
+    for out, tdt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        r = gemm.scaled_mm(A, B, sa, sb, bias=bias, out=out)
+        ref = v.to(tdt).view(torch.int16).numpy().view(np.uint16).astype(np.int32)
+        assert np.max(np.abs(r.bits.astype(np.int32) - ref)) <= 1
