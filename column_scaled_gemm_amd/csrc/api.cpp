@@ -179,15 +179,18 @@ int fp8sm_pick_variant(int64_t M, int64_t N, int64_t K) {
   return pick_from_table(M, N, K);
 }
 
-fp8sm_status fp8sm_scaled_mm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
-                             void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                             fp8sm_scale_kind ka, const void* sa, fp8sm_scale_kind kb,
-                             const void* sb, hipStream_t stream) {
+static fp8sm_status scaled_mm_impl(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                                   void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                   fp8sm_scale_kind ka, const void* sa, fp8sm_scale_kind kb,
+                                   const void* sb, const void* bias, fp8sm_dtype out,
+                                   hipStream_t stream) {
   const bool rowwise = (ka == FP8SM_KIND_TENSOR || ka == FP8SM_KIND_ROW) &&
                        (kb == FP8SM_KIND_TENSOR || kb == FP8SM_KIND_COL);
   const bool blockwise = (ka == FP8SM_KIND_GROUP128_UE8M0 || ka == FP8SM_KIND_GROUP128_FP32) &&
                          kb == FP8SM_KIND_BLOCK128;
   if (!rowwise && !blockwise) return FP8SM_ERR_UNSUPPORTED;
+  if (out != FP8SM_BF16 && out != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;
+  if (blockwise && (bias || out != FP8SM_BF16)) return FP8SM_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0) return FP8SM_ERR_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxK) return FP8SM_ERR_RANGE;
   if (lda < K || ldb < K || ldc < N) return FP8SM_ERR_SHAPE;
@@ -196,6 +199,7 @@ fp8sm_status fp8sm_scaled_mm(const uint8_t* A, int64_t lda, const uint8_t* B, in
   if (M == 0 || N == 0) return FP8SM_OK;
   if (!C) return FP8SM_ERR_NULL;
   if (!aligned(C, 16)) return FP8SM_ERR_ALIGN;
+  if (bias && !aligned(bias, 2)) return FP8SM_ERR_ALIGN;
   if (K > 0) {
     if (!A || !B || !sa || !sb) return FP8SM_ERR_NULL;
     if (!aligned(A, 16) || !aligned(B, 16)) return FP8SM_ERR_ALIGN;
@@ -205,7 +209,7 @@ fp8sm_status fp8sm_scaled_mm(const uint8_t* A, int64_t lda, const uint8_t* B, in
   fp8sm_status st = check_device();
   if (st != FP8SM_OK) return st;
   uint16_t* Cb = static_cast<uint16_t*>(C);
-  if (K == 0) return launched(launch_fill_zero_bf16(Cb, ldc, M, N, stream));
+  if (K == 0) return launched(launch_fill_k0(Cb, ldc, M, N, bias, stream));
   GemmArgs g;
   g.A = A;
   g.lda = lda;
@@ -220,10 +224,28 @@ fp8sm_status fp8sm_scaled_mm(const uint8_t* A, int64_t lda, const uint8_t* B, in
   g.sa_kind = (int)ka;
   g.sb = sb;
   g.sb_kind = (int)kb;
+  g.bias = bias;
+  g.out_f16 = out == FP8SM_FP16;
   if (blockwise) return launched(launch_gemm_blockwise(g, stream));
   int v = fp8sm_pick_variant(M, N, K);
   if (!variant_accepts(v, M)) return FP8SM_ERR_UNSUPPORTED;
   return launched(launch_gemm_rowwise(v, g, stream));
+}
+
+fp8sm_status fp8sm_scaled_mm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                             void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                             fp8sm_scale_kind ka, const void* sa, fp8sm_scale_kind kb,
+                             const void* sb, hipStream_t stream) {
+  return scaled_mm_impl(A, lda, B, ldb, C, ldc, M, N, K, ka, sa, kb, sb, nullptr, FP8SM_BF16,
+                        stream);
+}
+
+fp8sm_status fp8sm_scaled_mm_ex(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                                void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                fp8sm_scale_kind ka, const void* sa, fp8sm_scale_kind kb,
+                                const void* sb, const void* bias, fp8sm_dtype out,
+                                hipStream_t stream) {
+  return scaled_mm_impl(A, lda, B, ldb, C, ldc, M, N, K, ka, sa, kb, sb, bias, out, stream);
 }
 
 }  // extern "C"

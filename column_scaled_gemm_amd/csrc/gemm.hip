@@ -32,6 +32,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace fp8sm {
 
 constexpr int kChunk = 64;  // K bytes per pipeline stage / canonical chunk
@@ -159,18 +161,45 @@ __device__ __forceinline__ float rowwise_epilogue(float acc, float sa, float sb)
   return v * sb;
 }
 
+// Rowwise epilogue variants: EPI_F16 writes fp16 instead of bf16, EPI_BIAS
+// adds bias[c] (a value of the output dtype, widened exactly) in fp32 before
+// the final rounding: out = rnd(RN32(RN32(acc * sa) * sb) + bias).
+enum { EPI_F16 = 1, EPI_BIAS = 2 };
+
+template <int EPI>
+__device__ __forceinline__ uint16_t epi_round(float v) {
+  if constexpr ((EPI & EPI_F16) != 0)
+    return __builtin_bit_cast(uint16_t, (_Float16)v);  // RNE, overflow to inf
+  else
+    return f32_to_bf16_rne(v);
+}
+
+template <int EPI>
+__device__ __forceinline__ float epi_value(float acc, float sa, float sb,
+                                           const uint16_t* __restrict__ bias, int c) {
+  float v = rowwise_epilogue(acc, sa, sb);
+  if constexpr ((EPI & EPI_BIAS) != 0) {
+    if constexpr ((EPI & EPI_F16) != 0)
+      v = v + (float)__builtin_bit_cast(_Float16, bias[c]);
+    else
+      v = v + __uint_as_float((uint32_t)bias[c] << 16);
+  }
+  return v;
+}
+
 // Scale and store one lane's four consecutive outputs of row r (columns c..c+3,
 // c a multiple of 4; N % 8 == 0 so all four are in range when c < N).
+template <int EPI>
 __device__ __forceinline__ void store_row4(uint16_t* __restrict__ C, int64_t ldc, int r, int c,
                                            const f32x4& acc, float sar,
-                                           const float* __restrict__ sb, int sb_vec) {
-  float sbv[4];
+                                           const float* __restrict__ sb, int sb_vec,
+                                           const uint16_t* __restrict__ bias) {
+  uint16_t o[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) sbv[v] = sb[sb_vec ? c + v : 0];
-  const uint32_t lo = (uint32_t)f32_to_bf16_rne(rowwise_epilogue(acc[0], sar, sbv[0])) |
-                      ((uint32_t)f32_to_bf16_rne(rowwise_epilogue(acc[1], sar, sbv[1])) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16_rne(rowwise_epilogue(acc[2], sar, sbv[2])) |
-                      ((uint32_t)f32_to_bf16_rne(rowwise_epilogue(acc[3], sar, sbv[3])) << 16);
+  for (int v = 0; v < 4; ++v)
+    o[v] = epi_round<EPI>(epi_value<EPI>(acc[v], sar, sb[sb_vec ? c + v : 0], bias, c + v));
+  const uint32_t lo = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+  const uint32_t hi = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
   *reinterpret_cast<uint2*>(C + (int64_t)r * ldc + c) = make_uint2(lo, hi);
 }
 
@@ -232,11 +261,12 @@ __device__ __forceinline__ int frag32_off(int lane, int q) {
 // (wave tile BM/2 x BN/2), 64-wide K chunks in an NSLOT-slot LDS ring filled
 // by global->LDS DMA NSLOT-1 chunks ahead, one barrier per chunk.  OCC is the
 // number of workgroups meant to share a CU (their waits hide each other's).
-template <int BM, int BN, int NSLOT, int OCC>
+template <int BM, int BN, int NSLOT, int OCC, int EPI>
 __global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
-    int sa_vec, const float* __restrict__ sb, int sb_vec, int tiles_m, int tiles_n) {
+    int sa_vec, const float* __restrict__ sb, int sb_vec, const uint16_t* __restrict__ bias,
+    int tiles_m, int tiles_n) {
   constexpr int TM = BM / 32, TN = BN / 32;
   constexpr int ROWS = BM + BN;
   constexpr int SLOT = ROWS * kChunk;          // bytes per ring slot
@@ -319,7 +349,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int c = n0 + wn * (BN / 2) + 16 * j + 4 * g;
-      if (c < N) store_row4(C, ldc, r, c, acc[i][j], sar, sb, sb_vec);
+      if (c < N) store_row4<EPI>(C, ldc, r, c, acc[i][j], sar, sb, sb_vec, bias);
     }
   }
 }
@@ -503,11 +533,11 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 // chunks in flight.  A partial last chunk is loaded on its own: a lane's 16
 // bytes past K are read from the row's last 16 bytes, and its A values there
 // are zeroed before the multiply (B's duplicates then meet zeros).
-template <int TM, int D>
+template <int TM, int D, int EPI>
 __global__ __launch_bounds__(64) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
-    int sa_vec, const float* __restrict__ sb, int sb_vec) {
+    int sa_vec, const float* __restrict__ sb, int sb_vec, const uint16_t* __restrict__ bias) {
   const int lane = threadIdx.x;
   const int g = lane >> 4, r16 = lane & 15;
   const int n0 = blockIdx.x * 16;
@@ -578,7 +608,7 @@ __global__ __launch_bounds__(64) void gemm_decode_kernel(
     for (int v = 0; v < 4; ++v) {
       const int r = 16 * i + 4 * g + v;
       if (r < M)
-        C[(int64_t)r * ldc + c] = f32_to_bf16_rne(rowwise_epilogue(acc[i][0][v], sa[sa_vec ? r : 0], sbc));
+        C[(int64_t)r * ldc + c] = epi_round<EPI>(epi_value<EPI>(acc[i][0][v], sa[sa_vec ? r : 0], sbc, bias, c));
     }
 }
 
@@ -697,12 +727,15 @@ __global__ __launch_bounds__(256, 1) void gemm_blockwise_kernel(
   }
 }
 
-__global__ void fill_zero_bf16_kernel(uint16_t* C, int64_t ldc, int64_t M, int64_t N) {
+// K == 0: every accumulator is zero, so C = rnd(0 + bias) = bias (a value of
+// the output dtype) or +0.
+__global__ void fill_k0_kernel(uint16_t* C, int64_t ldc, int64_t M, int64_t N,
+                               const uint16_t* __restrict__ bias) {
   const int64_t total = M * N;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = i / N, c = i - r * N;
-    C[r * ldc + c] = 0;
+    C[r * ldc + c] = bias ? bias[c] : (uint16_t)0;
   }
 }
 
@@ -735,24 +768,42 @@ bool variant_accepts(int v, int64_t M) {
   }
 }
 
+// Runs f(std::integral_constant<int, EPI>) for the arguments' epilogue.
+template <typename Fn>
+static hipError_t with_epi(const GemmArgs& g, Fn&& f) {
+  switch ((g.out_f16 ? EPI_F16 : 0) | (g.bias ? EPI_BIAS : 0)) {
+    case 0: f(std::integral_constant<int, 0>{}); break;
+    case EPI_F16: f(std::integral_constant<int, EPI_F16>{}); break;
+    case EPI_BIAS: f(std::integral_constant<int, EPI_BIAS>{}); break;
+    default: f(std::integral_constant<int, EPI_F16 | EPI_BIAS>{}); break;
+  }
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int NSLOT, int OCC>
 static hipError_t launch_rowwise_tile(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_rowwise_kernel<BM, BN, NSLOT, OCC>), dim3(tiles_m * tiles_n), dim3(256), 0, s, g.A,
-                     g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
-                     static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
-                     static_cast<const float*>(g.sb), (int)(g.sb_kind == 2), tiles_m, tiles_n);
-  return hipGetLastError();
+  return with_epi(g, [&](auto e) {
+    constexpr int EPI = decltype(e)::value;
+    hipLaunchKernelGGL((gemm_rowwise_kernel<BM, BN, NSLOT, OCC, EPI>), dim3(tiles_m * tiles_n),
+                       dim3(256), 0, s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N,
+                       (int)g.K, static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
+                       static_cast<const float*>(g.sb), (int)(g.sb_kind == 2),
+                       static_cast<const uint16_t*>(g.bias), tiles_m, tiles_n);
+  });
 }
 
 template <int TM, int D>
 static hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
   const int grid = (int)((g.N + 15) / 16);
-  hipLaunchKernelGGL((gemm_decode_kernel<TM, D>), dim3(grid), dim3(64), 0, s, g.A, g.lda, g.B,
-                     g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
-                     static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
-                     static_cast<const float*>(g.sb), (int)(g.sb_kind == 2));
-  return hipGetLastError();
+  return with_epi(g, [&](auto e) {
+    constexpr int EPI = decltype(e)::value;
+    hipLaunchKernelGGL((gemm_decode_kernel<TM, D, EPI>), dim3(grid), dim3(64), 0, s, g.A, g.lda,
+                       g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
+                       static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
+                       static_cast<const float*>(g.sb), (int)(g.sb_kind == 2),
+                       static_cast<const uint16_t*>(g.bias));
+  });
 }
 
 hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
@@ -782,11 +833,13 @@ hipError_t launch_gemm_blockwise(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero_bf16(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s) {
+hipError_t launch_fill_k0(uint16_t* C, int64_t ldc, int64_t M, int64_t N, const void* bias,
+                          hipStream_t s) {
   int64_t blocks = (M * N + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_zero_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, C, ldc, M, N);
+  hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)blocks), dim3(256), 0, s, C, ldc, M, N,
+                     static_cast<const uint16_t*>(bias));
   return hipGetLastError();
 }
 

@@ -40,6 +40,8 @@ struct GemmArgs {
   int sa_kind;  // fp8sm_scale_kind
   const void* sb;
   int sb_kind;
+  const void* bias;  // rowwise / per-tensor only: output-dtype [N] or nullptr
+  int out_f16;       // rowwise / per-tensor only: fp16 output instead of bf16
 };
 
 // Rowwise / per-tensor variants.  All of them produce bitwise-identical rows.
@@ -57,6 +59,7 @@ const char* variant_name(int v);
 bool variant_accepts(int v, int64_t M);
 hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_blockwise(const GemmArgs& g, hipStream_t s);
-hipError_t launch_fill_zero_bf16(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s);
+hipError_t launch_fill_k0(uint16_t* C, int64_t ldc, int64_t M, int64_t N, const void* bias,
+                          hipStream_t s);
 
 }  // namespace fp8sm

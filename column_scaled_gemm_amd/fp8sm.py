@@ -33,6 +33,8 @@ SIGNATURES = {
     "fp8sm_quant_static": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i64, _p]),
     "fp8sm_quant_weight_block128": (_int, [_p, _int, _i64, _i64, _i64, _p, _i64, _p, _p]),
     "fp8sm_scaled_mm": (_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _int, _p, _int, _p, _p]),
+    "fp8sm_scaled_mm_ex": (_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _int, _p, _int, _p,
+                                  _p, _int, _p]),
     "fp8sm_silu_mul_f32": (_int, [_p, _int, _i64, _i64, _i64, _p, _i64, _p]),
     "fp8sm_scale_bytes": (ctypes.c_size_t, [_int, _int, _i64, _i64, _i32]),
     "fp8sm_status_str": (ctypes.c_char_p, [_int]),
@@ -182,14 +184,29 @@ def silu_mul_f32(x, y=None, stream=None):
     return y
 
 
-def scaled_mm(a, b, sa, sb, kind_a, kind_b, c=None, M=None, stream=None):
-    """a [M, K] uint8, b [N, K] uint8 (E4M3FN codes) -> c [M, N] bf16."""
+def scaled_mm(a, b, sa, sb, kind_a, kind_b, c=None, M=None, stream=None, bias=None,
+              out_dtype=None):
+    """a [M, K] uint8, b [N, K] uint8 (E4M3FN codes) -> c [M, N] bf16, or
+    fp16 with out_dtype=torch.float16; bias: optional [N] of the output dtype
+    (fp8sm_scaled_mm_ex)."""
     Mx, K = a.shape
     M = Mx if M is None else M
     N = b.shape[0]
+    if out_dtype is None:
+        out_dtype = c.dtype if c is not None else torch.bfloat16
     if c is None:
-        c = torch.empty((M, N), dtype=torch.bfloat16, device=b.device)
-    st = _load().fp8sm_scaled_mm(_ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(c), c.stride(0),
-                                 M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb), _stream(stream))
-    _check(st, "fp8sm_scaled_mm")
+        c = torch.empty((M, N), dtype=out_dtype, device=b.device)
+    if bias is None and out_dtype == torch.bfloat16:
+        st = _load().fp8sm_scaled_mm(_ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(c),
+                                     c.stride(0), M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb),
+                                     _stream(stream))
+        _check(st, "fp8sm_scaled_mm")
+        return c
+    out = {torch.bfloat16: BF16, torch.float16: FP16}[out_dtype]
+    if c.dtype != out_dtype or (bias is not None and bias.dtype != out_dtype):
+        raise Fp8smError("fp8sm_scaled_mm_ex: c and bias must have the output dtype")
+    st = _load().fp8sm_scaled_mm_ex(_ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(c), c.stride(0),
+                                    M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb),
+                                    None if bias is None else _ptr(bias), out, _stream(stream))
+    _check(st, "fp8sm_scaled_mm_ex")
     return c

@@ -163,6 +163,26 @@ fp8sm_status fp8sm_scaled_mm(const uint8_t* A, int64_t lda, const uint8_t* B, in
                              const void* sb, hipStream_t stream);
 
 /*
+ * Rowwise / per-tensor scaled GEMM with an optional bias and a bf16 or fp16
+ * output ([P2] Modifications: the deterministic FP8 linear is tested with
+ * bias, BF16/FP16 outputs, strided inputs and K tails; [P3] key source
+ * excerpts: the linear's apply() passes an optional bias):
+ *   C[m,n] = rnd( RN32( RN32(acc[m,n] * sa[m]) * sb[n] ) + bias[n] )
+ * bias: device [N] values of the output dtype (2-byte aligned), widened
+ * exactly to fp32 and added in fp32; NULL for none.  out: FP8SM_BF16 or
+ * FP8SM_FP16; rnd is round-to-nearest-even to that dtype (fp16 overflows to
+ * +-inf).  C holds that dtype.  Arguments, rules, reduction order and row
+ * invariance are those of fp8sm_scaled_mm, which equals this call with
+ * bias == NULL and out == FP8SM_BF16.  Blockwise scale kinds are accepted
+ * only with bias == NULL and out == FP8SM_BF16 (else FP8SM_ERR_UNSUPPORTED).
+ */
+fp8sm_status fp8sm_scaled_mm_ex(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                                void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                fp8sm_scale_kind ka, const void* sa, fp8sm_scale_kind kb,
+                                const void* sb, const void* bias, fp8sm_dtype out,
+                                hipStream_t stream);
+
+/*
  * The fused product alone, in fp32: y[m][k] = RN32(silu(x[m][k]) * x[m][K_out+k])
  * with the same silu as fp8sm_quant_group's FUSE_SILU_MUL ([P4] Modifications
  * 2).  x: device bf16/fp16 [M][ld_x], ld_x >= 2*K_out; y: device fp32

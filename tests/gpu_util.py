@@ -3,6 +3,7 @@ import numpy as np
 import torch
 
 from oracle import bf16 as obf16
+from oracle import fp16 as ofp16
 
 F32 = np.float32
 
@@ -31,10 +32,14 @@ def f32_bits(t):
 def tolerance_report(gpu_bits, res, K):
     """North-star GEMM bound: |gpu - oracle| <= 2^-7 |oracle| + 1e-3 sa sb sqrt(K).
 
+    The GPU bits are decoded in the oracle result's output dtype (bf16 or
+    fp16); equal values, infinities included, count as no error.
     Returns (violations, max err/tol, worst index)."""
-    gpu = obf16.bits_to_f64(gpu_bits)
+    dec = ofp16.bits_to_f64 if getattr(res, "dtype", "bf16") == "fp16" else obf16.bits_to_f64
+    gpu = dec(gpu_bits)
     ora = res.out
-    err = np.abs(gpu - ora)
+    with np.errstate(invalid="ignore"):
+        err = np.where(gpu == ora, 0.0, np.abs(gpu - ora))
     tol = 2.0 ** -7 * np.abs(ora) + 1e-3 * res.sab * np.sqrt(K)
     ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1), np.where(err > 0, np.inf, 0))
     idx = np.unravel_index(np.argmax(ratio), ratio.shape) if ratio.size else None

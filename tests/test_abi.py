@@ -72,6 +72,28 @@ def test_scaled_mm_rejects_bad_arguments_before_any_launch():
     assert _mm(lib, N=0, ldc=8) == E["OK"]
 
 
+def _mm_ex(lib, bias=0, out=0, **kw):
+    a = dict(A=16, lda=512, B=16, ldb=512, C=16, ldc=256, M=64, N=256, K=512, ka=1, sa=16, kb=2,
+             sb=16)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return lib.fp8sm_scaled_mm_ex(P(a["A"]), a["lda"], P(a["B"]), a["ldb"], P(a["C"]), a["ldc"],
+                                  a["M"], a["N"], a["K"], a["ka"], P(a["sa"]), a["kb"],
+                                  P(a["sb"]), P(bias), out, P(0))
+
+
+def test_scaled_mm_ex_rejects_bad_epilogues_before_any_launch():
+    from column_scaled_gemm_amd import fp8sm
+    lib = fp8sm.lib()
+    E = {v: k for k, v in fp8sm.STATUS.items()}
+    assert _mm_ex(lib, out=2) == E["ERR_UNSUPPORTED"]                    # bf16 / fp16 only
+    assert _mm_ex(lib, ka=3, kb=5, bias=16) == E["ERR_UNSUPPORTED"]      # blockwise: no bias
+    assert _mm_ex(lib, ka=3, kb=5, out=1) == E["ERR_UNSUPPORTED"]        # blockwise: bf16 only
+    assert _mm_ex(lib, bias=17) == E["ERR_ALIGN"]                        # 2-byte bias
+    assert _mm_ex(lib, K=100, bias=16, out=1) == E["ERR_ALIGN"]          # the shared rules hold
+    assert _mm_ex(lib, M=0, bias=16, out=1) == E["OK"]
+
+
 def test_quant_group_rejects_bad_arguments():
     from column_scaled_gemm_amd import fp8sm
     lib = fp8sm.lib()

@@ -127,6 +127,75 @@ def test_padded_leading_dimensions():
         assert torch.all(Cb[:, N:] == 3.0), fp8sm.variant_name(v)
 
 
+@pytest.mark.parametrize("shape", [(37, 264, 80), (100, 136, 208), (16, 48, 1552),
+                                   (257, 128, 4096)])
+@pytest.mark.parametrize("out,with_bias", [("fp16", False), ("bf16", True), ("fp16", True)])
+def test_bias_and_fp16_epilogues_every_variant(shape, out, with_bias):
+    # the epilogue of fp8sm_scaled_mm_ex against the oracle, bitwise equal
+    # across every variant the shape admits (decode and tiles); the plain bf16
+    # epilogue is the ragged-shape test above
+    M, N, K = shape
+    print(f"[case] epilogue M={M} N={N} K={K} out={out} bias={with_bias}", flush=True)
+    A, B, sa, sb = _quantized_case(M, N, K, seed=M + 2 * N + K)
+    tdt = torch.float16 if out == "fp16" else torch.bfloat16
+    bias_t = None
+    bias_v = None
+    if with_bias:
+        r = inputs.rng(M + N)
+        bias_t = torch.from_numpy(r.standard_normal(N).astype(F32) * F32(0.5)).to(tdt)
+        bias_v = bias_t.float().numpy().astype(np.float64)
+        bias_t = bias_t.to(cuda())
+    res = og.scaled_mm(A, B, sa, sb, bias=bias_v, out=out)
+    outs = {}
+    for v in _variants_for(M):
+        prev = fp8sm.force_variant(v)
+        try:
+            c = fp8sm.scaled_mm(to_gpu_u8(A), to_gpu_u8(B), to_gpu_f32(sa), to_gpu_f32(sb),
+                                fp8sm.KIND_ROW, fp8sm.KIND_COL, bias=bias_t, out_dtype=tdt)
+            torch.cuda.synchronize()
+        finally:
+            fp8sm.force_variant(prev)
+        outs[v] = bf16_bits(c)
+        assert_within_tolerance(outs[v], res, K, f"{shape} {out} bias={with_bias} "
+                                                 f"{fp8sm.variant_name(v)}")
+    first = next(iter(outs.values()))
+    for v, o in outs.items():
+        assert np.array_equal(o, first), f"variant {fp8sm.variant_name(v)} differs bitwise"
+
+
+def test_fp16_output_overflow_and_k0_bias():
+    # outputs past 65504 are +-inf in fp16, as in the oracle; K == 0 writes the
+    # bias row (C = rnd(0 + bias))
+    big = e4m3.encode(np.float32([448.0]))[0]
+    M, N, K = 5, 16, 64
+    A = np.full((M, K), big, np.uint8)
+    A[1] |= 0x80
+    B = np.full((N, K), big, np.uint8)
+    sb = np.full(N, 1.0, F32)
+    sb[8:] = 2.0 ** -10                                  # 64 * 448^2 / 1024 = 12544: finite
+    for v in _variants_for(M):
+        prev = fp8sm.force_variant(v)
+        try:
+            c = fp8sm.scaled_mm(to_gpu_u8(A), to_gpu_u8(B), to_gpu_f32(np.ones(M, F32)),
+                                to_gpu_f32(sb), fp8sm.KIND_ROW, fp8sm.KIND_COL,
+                                out_dtype=torch.float16)
+            torch.cuda.synchronize()
+        finally:
+            fp8sm.force_variant(prev)
+        got = c.float().cpu().numpy()
+        assert np.all(np.isposinf(got[0, :8])) and np.all(np.isneginf(got[1, :8]))
+        assert np.all(got[0, 8:] == 12544.0) and np.all(got[1, 8:] == -12544.0)
+    bias = torch.arange(16, dtype=torch.float16, device=cuda()) - 7.5
+    c = torch.full((3, 16), 9.0, dtype=torch.float16, device=cuda())
+    a0 = torch.zeros((3, 16), dtype=torch.uint8, device=cuda())
+    b0 = torch.zeros((16, 16), dtype=torch.uint8, device=cuda())
+    fp8sm.scaled_mm(a0[:, :0], b0[:, :0], to_gpu_f32(np.ones(3, F32)),
+                    to_gpu_f32(np.ones(16, F32)), fp8sm.KIND_ROW, fp8sm.KIND_COL, c=c,
+                    bias=bias, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert torch.equal(c, bias.expand(3, 16))
+
+
 def test_rows_do_not_depend_on_m():
     # sglang PR #44861 reviewers' check: rows of an M-row call against the same
     # rows inside a 101-row call, K = 6144, N = 5120
