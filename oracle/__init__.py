@@ -25,6 +25,12 @@ title and section):
                to bf16 ("Route large SM90 ..." Summary; PR #33148 digest,
                key source excerpts).
 * ``bf16``   -- round-to-nearest-even from float64 to bfloat16.
+* ``fp16``   -- round-to-nearest-even from float64 to IEEE half.
+* ``batched`` -- the batched / masked forms: each batch's live rows (a
+               per-batch count, clamped to the slab) go through the 2-D
+               definitions with that batch's operands (PR #33533 commit
+               messages and Speed Tests: the masked fused quant of the EP-MoE
+               path; sglang PR #44861 Modifications: strided 3-D inputs).
 
 Every function states which pins in ``tests/test_oracle_*.py`` tie it to
 something other than itself.
