@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/fp8sm.h"
@@ -46,6 +47,24 @@ inline fp8sm_status launched(hipError_t e) { return e == hipSuccess ? FP8SM_OK :
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxK = 65536;
+constexpr int64_t kMaxBatch = 65535;  // one grid row (blockIdx.y) per batch
+
+// Batch arguments common to every batched call: the count, non-negative
+// strides, and an int32-aligned row-count array (or NULL).
+fp8sm_status check_batch(int64_t nbatch, const int32_t* rows, std::initializer_list<int64_t> strides) {
+  if (nbatch < 0) return FP8SM_ERR_SHAPE;
+  if (nbatch > kMaxBatch) return FP8SM_ERR_RANGE;
+  for (int64_t st : strides)
+    if (st < 0) return FP8SM_ERR_SHAPE;
+  if (rows && !aligned(rows, 4)) return FP8SM_ERR_ALIGN;
+  return FP8SM_OK;
+}
+
+// Batches write disjoint outputs: a batch stride of an output at least spans
+// one batch's rows (rows - 1 strides of ld plus one row of `len`).
+inline bool disjoint(int64_t nbatch, int64_t stride, int64_t rows, int64_t ld, int64_t len) {
+  return nbatch <= 1 || rows == 0 || stride >= (rows - 1) * ld + len;
+}
 
 }  // namespace
 
@@ -77,10 +96,14 @@ size_t fp8sm_scale_bytes(fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, int64_t M,
   return (size_t)(rows * G * esz);
 }
 
-fp8sm_status fp8sm_quant_group(const void* x, fp8sm_dtype in, int64_t M, int64_t K_out,
-                               int64_t ld_x, int32_t group, uint32_t flags,
-                               fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, uint8_t* q,
-                               int64_t ld_q, void* scales, hipStream_t stream) {
+static fp8sm_status quant_group_impl(const void* x, fp8sm_dtype in, int64_t nbatch, int64_t M,
+                                     int64_t K_out, int64_t bs_x, int64_t ld_x,
+                                     const int32_t* rows, int32_t group, uint32_t flags,
+                                     fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, uint8_t* q,
+                                     int64_t bs_q, int64_t ld_q, void* scales,
+                                     hipStream_t stream) {
+  fp8sm_status bst = check_batch(nbatch, rows, {bs_x, bs_q});
+  if (bst != FP8SM_OK) return bst;
   if (in != FP8SM_BF16 && in != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;
   if (fmt != FP8SM_SCALE_FP32 && fmt != FP8SM_SCALE_UE8M0_FP32 && fmt != FP8SM_SCALE_UE8M0_BYTE)
     return FP8SM_ERR_UNSUPPORTED;
@@ -93,8 +116,9 @@ fp8sm_status fp8sm_quant_group(const void* x, fp8sm_dtype in, int64_t M, int64_t
   if (K_out % group) return FP8SM_ERR_SHAPE;
   const int64_t row_in = fused ? 2 * K_out : K_out;
   if (ld_x < row_in || ld_q < K_out) return FP8SM_ERR_SHAPE;
-  if (K_out % 8 || ld_x % 8 || ld_q % 8) return FP8SM_ERR_ALIGN;
-  if (M == 0) return FP8SM_OK;
+  if (K_out % 8 || ld_x % 8 || ld_q % 8 || bs_x % 8 || bs_q % 8) return FP8SM_ERR_ALIGN;
+  if (!disjoint(nbatch, bs_q, M, ld_q, K_out)) return FP8SM_ERR_SHAPE;
+  if (M == 0 || nbatch == 0) return FP8SM_OK;
   if (!x || !q || !scales) return FP8SM_ERR_NULL;
   if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scales, fmt == FP8SM_SCALE_UE8M0_BYTE ? 1 : 4))
     return FP8SM_ERR_ALIGN;
@@ -114,23 +138,62 @@ fp8sm_status fp8sm_quant_group(const void* x, fp8sm_dtype in, int64_t M, int64_t
   a.q = q;
   a.ld_q = ld_q;
   a.scales = scales;
+  const int64_t esz = fmt == FP8SM_SCALE_UE8M0_BYTE ? 1 : 4;
+  a.batch = QuantBatch{nbatch, bs_x, bs_q,
+                       (int64_t)fp8sm_scale_bytes(fmt, lay, M, K_out, group) / esz, rows};
   return launched(launch_quant_group(a, stream));
+}
+
+fp8sm_status fp8sm_quant_group(const void* x, fp8sm_dtype in, int64_t M, int64_t K_out,
+                               int64_t ld_x, int32_t group, uint32_t flags,
+                               fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, uint8_t* q,
+                               int64_t ld_q, void* scales, hipStream_t stream) {
+  return quant_group_impl(x, in, 1, M, K_out, 0, ld_x, nullptr, group, flags, fmt, lay, q, 0,
+                          ld_q, scales, stream);
+}
+
+fp8sm_status fp8sm_quant_group_batched(const void* x, fp8sm_dtype in, int64_t nbatch, int64_t M,
+                                       int64_t K_out, int64_t bs_x, int64_t ld_x,
+                                       const int32_t* rows, int32_t group, uint32_t flags,
+                                       fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, uint8_t* q,
+                                       int64_t bs_q, int64_t ld_q, void* scales,
+                                       hipStream_t stream) {
+  return quant_group_impl(x, in, nbatch, M, K_out, bs_x, ld_x, rows, group, flags, fmt, lay, q,
+                          bs_q, ld_q, scales, stream);
+}
+
+static fp8sm_status quant_static_impl(const void* x, fp8sm_dtype in, int64_t nbatch, int64_t M,
+                                      int64_t K, int64_t bs_x, int64_t ld_x, const float* scale,
+                                      uint8_t* q, int64_t bs_q, int64_t ld_q,
+                                      hipStream_t stream) {
+  fp8sm_status bst = check_batch(nbatch, nullptr, {bs_x, bs_q});
+  if (bst != FP8SM_OK) return bst;
+  if (in != FP8SM_BF16 && in != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;
+  if (M < 0 || K <= 0) return FP8SM_ERR_SHAPE;
+  if (M > kMaxDim || K > kMaxDim) return FP8SM_ERR_RANGE;
+  if (ld_x < K || ld_q < K) return FP8SM_ERR_SHAPE;
+  if (K % 8 || ld_x % 8 || ld_q % 8 || bs_x % 8 || bs_q % 8) return FP8SM_ERR_ALIGN;
+  if (!disjoint(nbatch, bs_q, M, ld_q, K)) return FP8SM_ERR_SHAPE;
+  if (M == 0 || nbatch == 0) return FP8SM_OK;
+  if (!x || !q || !scale) return FP8SM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 4)) return FP8SM_ERR_ALIGN;
+  fp8sm_status st = check_device();
+  if (st != FP8SM_OK) return st;
+  return launched(launch_quant_static(x, in == FP8SM_FP16, M, K, ld_x, scale, q, ld_q, stream,
+                                      QuantBatch{nbatch, bs_x, bs_q, 0, nullptr}));
 }
 
 fp8sm_status fp8sm_quant_static(const void* x, fp8sm_dtype in, int64_t M, int64_t K,
                                 int64_t ld_x, const float* scale, uint8_t* q, int64_t ld_q,
                                 hipStream_t stream) {
-  if (in != FP8SM_BF16 && in != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;
-  if (M < 0 || K <= 0) return FP8SM_ERR_SHAPE;
-  if (M > kMaxDim || K > kMaxDim) return FP8SM_ERR_RANGE;
-  if (ld_x < K || ld_q < K) return FP8SM_ERR_SHAPE;
-  if (K % 8 || ld_x % 8 || ld_q % 8) return FP8SM_ERR_ALIGN;
-  if (M == 0) return FP8SM_OK;
-  if (!x || !q || !scale) return FP8SM_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 4)) return FP8SM_ERR_ALIGN;
-  fp8sm_status st = check_device();
-  if (st != FP8SM_OK) return st;
-  return launched(launch_quant_static(x, in == FP8SM_FP16, M, K, ld_x, scale, q, ld_q, stream));
+  return quant_static_impl(x, in, 1, M, K, 0, ld_x, scale, q, 0, ld_q, stream);
+}
+
+fp8sm_status fp8sm_quant_static_batched(const void* x, fp8sm_dtype in, int64_t nbatch, int64_t M,
+                                        int64_t K, int64_t bs_x, int64_t ld_x,
+                                        const float* scale, uint8_t* q, int64_t bs_q,
+                                        int64_t ld_q, hipStream_t stream) {
+  return quant_static_impl(x, in, nbatch, M, K, bs_x, ld_x, scale, q, bs_q, ld_q, stream);
 }
 
 fp8sm_status fp8sm_quant_weight_block128(const void* w, fp8sm_dtype in, int64_t N, int64_t K,
@@ -183,7 +246,10 @@ static fp8sm_status scaled_mm_impl(const uint8_t* A, int64_t lda, const uint8_t*
                                    void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                                    fp8sm_scale_kind ka, const void* sa, fp8sm_scale_kind kb,
                                    const void* sb, const void* bias, fp8sm_dtype out,
-                                   hipStream_t stream) {
+                                   hipStream_t stream,
+                                   const GemmBatch& bt = GemmBatch{1, 0, 0, 0, 0, 0, nullptr}) {
+  fp8sm_status bst = check_batch(bt.count, bt.rows, {bt.a, bt.b, bt.c, bt.sa, bt.sb});
+  if (bst != FP8SM_OK) return bst;
   const bool rowwise = (ka == FP8SM_KIND_TENSOR || ka == FP8SM_KIND_ROW) &&
                        (kb == FP8SM_KIND_TENSOR || kb == FP8SM_KIND_COL);
   const bool blockwise = (ka == FP8SM_KIND_GROUP128_UE8M0 || ka == FP8SM_KIND_GROUP128_FP32) &&
@@ -194,9 +260,10 @@ static fp8sm_status scaled_mm_impl(const uint8_t* A, int64_t lda, const uint8_t*
   if (M < 0 || N < 0 || K < 0) return FP8SM_ERR_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxK) return FP8SM_ERR_RANGE;
   if (lda < K || ldb < K || ldc < N) return FP8SM_ERR_SHAPE;
-  if (K % 16 || lda % 16 || ldb % 16) return FP8SM_ERR_ALIGN;
-  if (N % 8 || ldc % 8) return FP8SM_ERR_ALIGN;
-  if (M == 0 || N == 0) return FP8SM_OK;
+  if (K % 16 || lda % 16 || ldb % 16 || bt.a % 16 || bt.b % 16) return FP8SM_ERR_ALIGN;
+  if (N % 8 || ldc % 8 || bt.c % 8) return FP8SM_ERR_ALIGN;
+  if (!disjoint(bt.count, bt.c, M, ldc, N)) return FP8SM_ERR_SHAPE;
+  if (M == 0 || N == 0 || bt.count == 0) return FP8SM_OK;
   if (!C) return FP8SM_ERR_NULL;
   if (!aligned(C, 16)) return FP8SM_ERR_ALIGN;
   if (bias && !aligned(bias, 2)) return FP8SM_ERR_ALIGN;
@@ -209,7 +276,7 @@ static fp8sm_status scaled_mm_impl(const uint8_t* A, int64_t lda, const uint8_t*
   fp8sm_status st = check_device();
   if (st != FP8SM_OK) return st;
   uint16_t* Cb = static_cast<uint16_t*>(C);
-  if (K == 0) return launched(launch_fill_k0(Cb, ldc, M, N, bias, stream));
+  if (K == 0) return launched(launch_fill_k0(Cb, ldc, M, N, bias, stream, bt));
   GemmArgs g;
   g.A = A;
   g.lda = lda;
@@ -226,6 +293,7 @@ static fp8sm_status scaled_mm_impl(const uint8_t* A, int64_t lda, const uint8_t*
   g.sb_kind = (int)kb;
   g.bias = bias;
   g.out_f16 = out == FP8SM_FP16;
+  g.batch = bt;
   if (blockwise) return launched(launch_gemm_blockwise(g, stream));
   int v = fp8sm_pick_variant(M, N, K);
   if (!variant_accepts(v, M)) return FP8SM_ERR_UNSUPPORTED;
@@ -246,6 +314,17 @@ fp8sm_status fp8sm_scaled_mm_ex(const uint8_t* A, int64_t lda, const uint8_t* B,
                                 const void* sb, const void* bias, fp8sm_dtype out,
                                 hipStream_t stream) {
   return scaled_mm_impl(A, lda, B, ldb, C, ldc, M, N, K, ka, sa, kb, sb, bias, out, stream);
+}
+
+fp8sm_status fp8sm_scaled_mm_batched(int64_t nbatch, const int32_t* rows, const uint8_t* A,
+                                     int64_t bs_a, int64_t lda, const uint8_t* B, int64_t bs_b,
+                                     int64_t ldb, void* C, int64_t bs_c, int64_t ldc, int64_t M,
+                                     int64_t N, int64_t K, fp8sm_scale_kind ka, const void* sa,
+                                     int64_t bs_sa, fp8sm_scale_kind kb, const void* sb,
+                                     int64_t bs_sb, const void* bias, fp8sm_dtype out,
+                                     hipStream_t stream) {
+  return scaled_mm_impl(A, lda, B, ldb, C, ldc, M, N, K, ka, sa, kb, sb, bias, out, stream,
+                        GemmBatch{nbatch, bs_a, bs_b, bs_c, bs_sa, bs_sb, rows});
 }
 
 }  // extern "C"

@@ -92,4 +92,12 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Live rows of this workgroup's batch (blockIdx.y): clamp(rows[b], 0, M), or
+// M when there are no per-batch counts.  Uniform over the workgroup.
+__device__ __forceinline__ int64_t batch_rows(const int32_t* rows, int64_t M) {
+  if (rows == nullptr) return M;
+  const int64_t r = rows[blockIdx.y];
+  return r < 0 ? 0 : (r > M ? M : r);
+}
+
 }  // namespace fp8sm

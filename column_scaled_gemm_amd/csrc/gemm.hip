@@ -32,6 +32,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace fp8sm {
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
     int sa_vec, const float* __restrict__ sb, int sb_vec, const uint16_t* __restrict__ bias,
-    int tiles_m, int tiles_n) {
+    int tiles_m, int tiles_n, GemmBatch gb) {
   constexpr int TM = BM / 32, TN = BN / 32;
   constexpr int ROWS = BM + BN;
   constexpr int SLOT = ROWS * kChunk;          // bytes per ring slot
@@ -279,6 +280,16 @@ __global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  {
+    const int64_t bi = blockIdx.y;
+    A += bi * gb.a;
+    B += bi * gb.b;
+    C += bi * gb.c;
+    sa += bi * gb.sa;
+    sb += bi * gb.sb;
+    M = (int)batch_rows(gb.rows, M);
+    if (m0 >= M) return;  // the whole workgroup, before any barrier
+  }
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1;
@@ -377,7 +388,7 @@ template <int NSLOT, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const uint8_t* __restrict__ ea,
-    const float* __restrict__ sbb, int tiles_m, int tiles_n) {
+    const float* __restrict__ sbb, int tiles_m, int tiles_n, GemmBatch gb) {
   constexpr int BM = 128, BN = 128, TM = 2, TN = 2;  // 32-row subtiles per wavefront
   constexpr int ROWS = BM + BN;
   constexpr int SLOT = ROWS * kChunk;
@@ -391,6 +402,16 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  {
+    const int64_t bi = blockIdx.y;
+    A += bi * gb.a;
+    B += bi * gb.b;
+    C += bi * gb.c;
+    ea += bi * gb.sa;
+    sbb += bi * gb.sb;
+    M = (int)batch_rows(gb.rows, M);
+    if (m0 >= M) return;  // the whole workgroup, before any barrier
+  }
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1;
@@ -537,7 +558,18 @@ template <int TM, int D, int EPI>
 __global__ __launch_bounds__(64) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
-    int sa_vec, const float* __restrict__ sb, int sb_vec, const uint16_t* __restrict__ bias) {
+    int sa_vec, const float* __restrict__ sb, int sb_vec, const uint16_t* __restrict__ bias,
+    GemmBatch gb) {
+  {
+    const int64_t bi = blockIdx.y;
+    A += bi * gb.a;
+    B += bi * gb.b;
+    C += bi * gb.c;
+    sa += bi * gb.sa;
+    sb += bi * gb.sb;
+    M = (int)batch_rows(gb.rows, M);
+    if (M == 0) return;
+  }
   const int lane = threadIdx.x;
   const int g = lane >> 4, r16 = lane & 15;
   const int n0 = blockIdx.x * 16;
@@ -622,13 +654,23 @@ template <bool UE8M0>
 __global__ __launch_bounds__(256, 1) void gemm_blockwise_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const void* __restrict__ sa_p,
-    const float* __restrict__ sb_p, int tiles_m, int tiles_n) {
+    const float* __restrict__ sb_p, int tiles_m, int tiles_n, GemmBatch gb) {
   constexpr int BM = 128, BN = 128, TM = 4, TN = 4;
   constexpr int ROWS = BM + BN, CPT = ROWS * 8 / 256, STAGE = ROWS * 128;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  {
+    const int64_t bi = blockIdx.y;
+    A += bi * gb.a;
+    B += bi * gb.b;
+    C += bi * gb.c;
+    sa_p = static_cast<const uint8_t*>(sa_p) + bi * gb.sa * (UE8M0 ? 1 : 4);
+    sb_p += bi * gb.sb;
+    M = (int)batch_rows(gb.rows, M);
+    if (m0 >= M) return;  // the whole workgroup, before any barrier
+  }
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int g = lane >> 4, r16 = lane & 15;
@@ -730,7 +772,9 @@ __global__ __launch_bounds__(256, 1) void gemm_blockwise_kernel(
 // K == 0: every accumulator is zero, so C = rnd(0 + bias) = bias (a value of
 // the output dtype) or +0.
 __global__ void fill_k0_kernel(uint16_t* C, int64_t ldc, int64_t M, int64_t N,
-                               const uint16_t* __restrict__ bias) {
+                               const uint16_t* __restrict__ bias, GemmBatch gb) {
+  C += (int64_t)blockIdx.y * gb.c;
+  M = batch_rows(gb.rows, M);
   const int64_t total = M * N;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -768,6 +812,10 @@ bool variant_accepts(int v, int64_t M) {
   }
 }
 
+static dim3 grid2(int64_t blocks, const GemmArgs& g) {
+  return dim3((unsigned)blocks, (unsigned)g.batch.count);
+}
+
 // Runs f(std::integral_constant<int, EPI>) for the arguments' epilogue.
 template <typename Fn>
 static hipError_t with_epi(const GemmArgs& g, Fn&& f) {
@@ -785,11 +833,11 @@ static hipError_t launch_rowwise_tile(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
   return with_epi(g, [&](auto e) {
     constexpr int EPI = decltype(e)::value;
-    hipLaunchKernelGGL((gemm_rowwise_kernel<BM, BN, NSLOT, OCC, EPI>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((gemm_rowwise_kernel<BM, BN, NSLOT, OCC, EPI>), grid2(tiles_m * tiles_n, g),
                        dim3(256), 0, s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N,
                        (int)g.K, static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
                        static_cast<const float*>(g.sb), (int)(g.sb_kind == 2),
-                       static_cast<const uint16_t*>(g.bias), tiles_m, tiles_n);
+                       static_cast<const uint16_t*>(g.bias), tiles_m, tiles_n, g.batch);
   });
 }
 
@@ -798,11 +846,11 @@ static hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
   const int grid = (int)((g.N + 15) / 16);
   return with_epi(g, [&](auto e) {
     constexpr int EPI = decltype(e)::value;
-    hipLaunchKernelGGL((gemm_decode_kernel<TM, D, EPI>), dim3(grid), dim3(64), 0, s, g.A, g.lda,
-                       g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
+    hipLaunchKernelGGL((gemm_decode_kernel<TM, D, EPI>), grid2(grid, g), dim3(64), 0, s, g.A,
+                       g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
                        static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
                        static_cast<const float*>(g.sb), (int)(g.sb_kind == 2),
-                       static_cast<const uint16_t*>(g.bias));
+                       static_cast<const uint16_t*>(g.bias), g.batch);
   });
 }
 
@@ -822,24 +870,25 @@ hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
 hipError_t launch_gemm_blockwise(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (int)((g.M + 127) / 128), tiles_n = (int)((g.N + 127) / 128);
   if (g.sa_kind == 3)
-    hipLaunchKernelGGL((gemm_block_ue8m0_kernel<4, 2>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
-                       g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
+    hipLaunchKernelGGL((gemm_block_ue8m0_kernel<4, 2>), grid2(tiles_m * tiles_n, g), dim3(256),
+                       0, s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
                        static_cast<const uint8_t*>(g.sa), static_cast<const float*>(g.sb), tiles_m,
-                       tiles_n);
+                       tiles_n, g.batch);
   else
-    hipLaunchKernelGGL((gemm_blockwise_kernel<false>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
-                       g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, g.sa,
-                       static_cast<const float*>(g.sb), tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_blockwise_kernel<false>), grid2(tiles_m * tiles_n, g), dim3(256), 0,
+                       s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, g.sa,
+                       static_cast<const float*>(g.sb), tiles_m, tiles_n, g.batch);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_k0(uint16_t* C, int64_t ldc, int64_t M, int64_t N, const void* bias,
-                          hipStream_t s) {
+                          hipStream_t s, const GemmBatch& bt) {
   int64_t blocks = (M * N + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)blocks), dim3(256), 0, s, C, ldc, M, N,
-                     static_cast<const uint16_t*>(bias));
+  const int64_t cap = std::max<int64_t>(1, 65536 / std::max<int64_t>(1, bt.count));
+  if (blocks > cap) blocks = cap;
+  if (blocks == 0 || bt.count == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)blocks, (unsigned)bt.count), dim3(256), 0, s,
+                     C, ldc, M, N, static_cast<const uint16_t*>(bias), bt);
   return hipGetLastError();
 }
 

@@ -1,10 +1,32 @@
 // Internal launcher interface between the C-ABI layer (api.cpp) and the
-// kernels (quant.hip, gemm.hip).  Host code only; no HIP device code here.
+// kernels (quant.hip, gemm.hip).  No device code here; the two batch structs
+// are also passed to kernels by value.
 #pragma once
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace fp8sm {
+
+// A batch of problems of one shape, one per blockIdx.y: batch b reads and
+// writes every operand at its base + b * that operand's stride; when `rows`
+// is set (device int32 [count]) batch b has clamp(rows[b], 0, M) live rows and
+// its other rows are left untouched.  A plain 2-D call is count 1, strides 0,
+// rows null.
+struct QuantBatch {
+  int64_t count;
+  int64_t sx;  // x, elements
+  int64_t sq;  // q, bytes
+  int64_t ss;  // scales, scale elements (bytes for UE8M0 bytes, floats otherwise)
+  const int32_t* rows;
+};
+
+struct GemmBatch {
+  int64_t count;
+  int64_t a, b;    // A, B: bytes (b = 0: one weight for every batch)
+  int64_t c;       // C: output elements
+  int64_t sa, sb;  // scales: elements of their kind (0: shared)
+  const int32_t* rows;
+};
 
 struct QuantArgs {
   const void* x;
@@ -18,11 +40,13 @@ struct QuantArgs {
   uint8_t* q;
   int64_t ld_q;
   void* scales;
+  QuantBatch batch{1, 0, 0, 0, nullptr};
 };
 
 hipError_t launch_quant_group(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_static(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x,
-                               const float* scale, uint8_t* q, int64_t ld_q, hipStream_t s);
+                               const float* scale, uint8_t* q, int64_t ld_q, hipStream_t s,
+                               const QuantBatch& bt = QuantBatch{1, 0, 0, 0, nullptr});
 hipError_t launch_silu_mul(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x, float* y,
                            int64_t ld_y, hipStream_t s);
 hipError_t launch_quant_wblock(const void* w, bool f16, int64_t N, int64_t K, int64_t ld_w,
@@ -42,6 +66,7 @@ struct GemmArgs {
   int sb_kind;
   const void* bias;  // rowwise / per-tensor only: output-dtype [N] or nullptr
   int out_f16;       // rowwise / per-tensor only: fp16 output instead of bf16
+  GemmBatch batch{1, 0, 0, 0, 0, 0, nullptr};
 };
 
 // Rowwise / per-tensor variants.  All of them produce bitwise-identical rows.
@@ -60,6 +85,6 @@ bool variant_accepts(int v, int64_t M);
 hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_blockwise(const GemmArgs& g, hipStream_t s);
 hipError_t launch_fill_k0(uint16_t* C, int64_t ldc, int64_t M, int64_t N, const void* bias,
-                          hipStream_t s);
+                          hipStream_t s, const GemmBatch& bt = GemmBatch{1, 0, 0, 0, 0, 0, nullptr});
 
 }  // namespace fp8sm

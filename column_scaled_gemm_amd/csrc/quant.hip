@@ -50,6 +50,20 @@ __device__ __forceinline__ void store_scale(void* scales, int64_t idx, float v, 
   }
 }
 
+// Moves a workgroup's x, q and scale pointers to its batch (blockIdx.y) and
+// returns the batch's live rows.
+template <int FMT>
+__device__ __forceinline__ int64_t enter_batch(const QuantBatch& bt,
+                                               const uint16_t* __restrict__& x,
+                                               uint8_t* __restrict__& q,
+                                               void* __restrict__& scales, int64_t M) {
+  const int64_t b = blockIdx.y;
+  x += b * bt.sx;
+  q += b * bt.sq;
+  scales = static_cast<uint8_t*>(scales) + b * bt.ss * (FMT == FMT_UE8M0_BYTE ? 1 : 4);
+  return batch_rows(bt.rows, M);
+}
+
 // y = silu(gate) * up in fp32 (fused) or the widened input; `tab` is the
 // workgroup's silu table (fused only).
 template <bool F16, bool FUSED>
@@ -130,7 +144,8 @@ template <bool F16, int FMT>
 __global__ __launch_bounds__(256) void quant_g128_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t G, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, int mn_major,
-    int64_t mpad) {
+    int64_t mpad, QuantBatch bt) {
+  M = enter_batch<FMT>(bt, x, q, scales, M);
   const int lane = threadIdx.x & 63;
   const int quarter = lane >> 4;
   const int l16 = lane & 15;
@@ -176,8 +191,10 @@ template <bool F16, int FMT, bool O32>
 __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
     const uint16_t* __restrict__ x, int M, int G, int64_t K, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, int mn_major,
-    int64_t mpad) {
+    int64_t mpad, QuantBatch bt) {
   __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
+  M = (int)enter_batch<FMT>(bt, x, q, scales, M);
+  if (M == 0) return;  // the whole workgroup: M is uniform
   const int lane = threadIdx.x & 63;
   const int quarter = lane >> 4;
   const int l16 = lane & 15;
@@ -260,7 +277,8 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
 template <bool F16, int NC, int NFULL, int FMT>
 __global__ __launch_bounds__(256) void quant_token_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, QuantBatch bt) {
+  M = enter_batch<FMT>(bt, x, q, scales, M);
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
   int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -334,8 +352,9 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
 template <bool F16, int NCW, int FMT>
 __global__ __launch_bounds__(256) void quant_token_wg_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, QuantBatch bt) {
   __shared__ float part[2][4];
+  M = enter_batch<FMT>(bt, x, q, scales, M);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nch = (int)(K >> 3);  // K <= 2^30
@@ -442,7 +461,8 @@ __device__ __forceinline__ void quant_row_2pass(const uint16_t* __restrict__ xr,
 template <bool F16, int FMT>
 __global__ __launch_bounds__(256) void quant_token_2pass_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, QuantBatch bt) {
+  M = enter_batch<FMT>(bt, x, q, scales, M);
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;  // whole wavefront; the kernel has no barrier
   quant_row_2pass<F16, false, FMT>(x + row * ld_x, K, q + row * ld_q, scales, row,
@@ -452,8 +472,10 @@ __global__ __launch_bounds__(256) void quant_token_2pass_kernel(
 template <bool F16, int FMT>
 __global__ __launch_bounds__(1024) void quant_token_fused_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales) {
+    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, QuantBatch bt) {
   __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
+  M = enter_batch<FMT>(bt, x, q, scales, M);
+  if (M == 0) return;  // the whole workgroup: M is uniform
   SiluTable<F16>::build(tab, threadIdx.x, 1024);
   __syncthreads();
   for (int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6); row < M;
@@ -468,7 +490,10 @@ __global__ __launch_bounds__(1024) void quant_token_fused_kernel(
 template <bool F16>
 __global__ __launch_bounds__(256) void quant_static_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
-    const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ld_q) {
+    const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ld_q, QuantBatch bt) {
+  x += (int64_t)blockIdx.y * bt.sx;
+  q += (int64_t)blockIdx.y * bt.sq;
+  M = batch_rows(bt.rows, M);
   const int64_t nch = K >> 3;
   const int64_t total = M * nch;
   const float inv = 1.0f / scale[0];
@@ -589,9 +614,18 @@ static int cu_count() {
   return n;
 }
 
-static unsigned persistent_blocks(int64_t work_per_block_units, int64_t units) {
+// Workgroups per batch for a persistent kernel: enough for the work, at most
+// `cap` over all batches together (at least one per batch).
+static unsigned persistent_blocks(int64_t work_per_block_units, int64_t units, int64_t batches = 1,
+                                  int64_t cap = 0) {
+  if (cap <= 0) cap = cu_count();
   const int64_t need = (units + work_per_block_units - 1) / work_per_block_units;
-  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(need, cu_count()));
+  const int64_t share = (cap + batches - 1) / batches;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(need, share));
+}
+
+static dim3 grid2(int64_t blocks, const QuantBatch& bt) {
+  return dim3((unsigned)blocks, (unsigned)bt.count);
 }
 
 template <bool F16>
@@ -601,16 +635,16 @@ static hipError_t launch_g128(int fmt, const QuantArgs& a, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   return with_fmt(fmt, [&](auto f) {
     constexpr int FMT = decltype(f)::value;
-    hipLaunchKernelGGL((quant_g128_kernel<F16, FMT>), dim3((unsigned)((waves + 3) / 4)),
-                       dim3(256), 0, s, x, a.M, G, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major,
-                       a.mpad);
+    hipLaunchKernelGGL((quant_g128_kernel<F16, FMT>), grid2((waves + 3) / 4, a.batch), dim3(256),
+                       0, s, x, a.M, G, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad,
+                       a.batch);
   });
 }
 
 template <bool F16>
 static hipError_t launch_g128_fused(int fmt, const QuantArgs& a, hipStream_t s) {
   const int64_t G = a.K / 128;
-  const unsigned blocks = persistent_blocks(16 * 16, a.M * G);  // 16 waves x 16 groups
+  const unsigned blocks = persistent_blocks(16 * 16, a.M * G, a.batch.count);  // 16 waves x 16 groups
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   // every byte offset the kernel forms below 2^32: 32-bit address arithmetic
   const uint64_t lim = (uint64_t)1 << 32;
@@ -620,13 +654,13 @@ static hipError_t launch_g128_fused(int fmt, const QuantArgs& a, hipStream_t s) 
   return with_fmt(fmt, [&](auto f) {
     constexpr int FMT = decltype(f)::value;
     if (o32)
-      hipLaunchKernelGGL((quant_g128_fused_kernel<F16, FMT, true>), dim3(blocks), dim3(1024), 0,
-                         s, x, (int)a.M, (int)G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major,
-                         a.mpad);
+      hipLaunchKernelGGL((quant_g128_fused_kernel<F16, FMT, true>), grid2(blocks, a.batch),
+                         dim3(1024), 0, s, x, (int)a.M, (int)G, a.K, a.ld_x, a.q, a.ld_q,
+                         a.scales, a.mn_major, a.mpad, a.batch);
     else
-      hipLaunchKernelGGL((quant_g128_fused_kernel<F16, FMT, false>), dim3(blocks), dim3(1024), 0,
-                         s, x, (int)a.M, (int)G, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major,
-                         a.mpad);
+      hipLaunchKernelGGL((quant_g128_fused_kernel<F16, FMT, false>), grid2(blocks, a.batch),
+                         dim3(1024), 0, s, x, (int)a.M, (int)G, a.K, a.ld_x, a.q, a.ld_q,
+                         a.scales, a.mn_major, a.mpad, a.batch);
   });
 }
 
@@ -650,9 +684,9 @@ static hipError_t launch_token_nc(int fmt, const QuantArgs& a, hipStream_t s) {
     constexpr int FMT = decltype(f)::value;
     static std::atomic<int> occ{0};
     const int per_cu = resident_blocks(quant_token_kernel<F16, NC, NFULL, FMT>, occ);
-    const int64_t blocks = std::min<int64_t>((a.M + 3) / 4, (int64_t)per_cu * cu_count());
-    hipLaunchKernelGGL((quant_token_kernel<F16, NC, NFULL, FMT>), dim3((unsigned)blocks),
-                       dim3(256), 0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+    const int64_t blocks = persistent_blocks(4, a.M, a.batch.count, (int64_t)per_cu * cu_count());
+    hipLaunchKernelGGL((quant_token_kernel<F16, NC, NFULL, FMT>), grid2(blocks, a.batch),
+                       dim3(256), 0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.batch);
   });
 }
 
@@ -661,19 +695,19 @@ static hipError_t launch_token_2pass(int fmt, const QuantArgs& a, hipStream_t s)
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   return with_fmt(fmt, [&](auto f) {
     constexpr int FMT = decltype(f)::value;
-    hipLaunchKernelGGL((quant_token_2pass_kernel<F16, FMT>), dim3((unsigned)((a.M + 3) / 4)),
-                       dim3(256), 0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+    hipLaunchKernelGGL((quant_token_2pass_kernel<F16, FMT>), grid2((a.M + 3) / 4, a.batch),
+                       dim3(256), 0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.batch);
   });
 }
 
 template <bool F16>
 static hipError_t launch_token_fused(int fmt, const QuantArgs& a, hipStream_t s) {
-  const unsigned blocks = persistent_blocks(16, a.M);  // one row per wavefront
+  const unsigned blocks = persistent_blocks(16, a.M, a.batch.count);  // one row per wavefront
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   return with_fmt(fmt, [&](auto f) {
     constexpr int FMT = decltype(f)::value;
-    hipLaunchKernelGGL((quant_token_fused_kernel<F16, FMT>), dim3(blocks), dim3(1024), 0, s, x,
-                       a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+    hipLaunchKernelGGL((quant_token_fused_kernel<F16, FMT>), grid2(blocks, a.batch), dim3(1024),
+                       0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.batch);
   });
 }
 
@@ -684,9 +718,9 @@ static hipError_t launch_token_wg(int fmt, const QuantArgs& a, hipStream_t s) {
     constexpr int FMT = decltype(f)::value;
     static std::atomic<int> occ{0};
     const int per_cu = resident_blocks(quant_token_wg_kernel<F16, NCW, FMT>, occ);
-    const int64_t blocks = std::min<int64_t>(a.M, (int64_t)per_cu * cu_count());
-    hipLaunchKernelGGL((quant_token_wg_kernel<F16, NCW, FMT>), dim3((unsigned)blocks), dim3(256),
-                       0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales);
+    const int64_t blocks = persistent_blocks(1, a.M, a.batch.count, (int64_t)per_cu * cu_count());
+    hipLaunchKernelGGL((quant_token_wg_kernel<F16, NCW, FMT>), grid2(blocks, a.batch), dim3(256),
+                       0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.batch);
   });
 }
 
@@ -709,7 +743,7 @@ static hipError_t launch_token(int fmt, const QuantArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_quant_group(const QuantArgs& a, hipStream_t s) {
-  if (a.M == 0) return hipSuccess;
+  if (a.M == 0 || a.batch.count == 0) return hipSuccess;
   const bool per_token = a.group == a.K;
   if (per_token) {
     if (a.fused) return a.f16 ? launch_token_fused<true>(a.fmt, a, s)
@@ -722,18 +756,20 @@ hipError_t launch_quant_group(const QuantArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_quant_static(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x,
-                               const float* scale, uint8_t* q, int64_t ld_q, hipStream_t s) {
-  if (M == 0) return hipSuccess;
+                               const float* scale, uint8_t* q, int64_t ld_q, hipStream_t s,
+                               const QuantBatch& bt) {
+  if (M == 0 || bt.count == 0) return hipSuccess;
   const int64_t chunks = M * (K / 8);
   int64_t blocks = (chunks + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  const int64_t cap = std::max<int64_t>(1, 65536 / bt.count);
+  if (blocks > cap) blocks = cap;
   const uint16_t* xx = static_cast<const uint16_t*>(x);
   if (f16)
-    hipLaunchKernelGGL((quant_static_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, xx,
-                       M, K, ld_x, scale, q, ld_q);
+    hipLaunchKernelGGL((quant_static_kernel<true>), grid2(blocks, bt), dim3(256), 0, s, xx, M, K,
+                       ld_x, scale, q, ld_q, bt);
   else
-    hipLaunchKernelGGL((quant_static_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, xx,
-                       M, K, ld_x, scale, q, ld_q);
+    hipLaunchKernelGGL((quant_static_kernel<false>), grid2(blocks, bt), dim3(256), 0, s, xx, M,
+                       K, ld_x, scale, q, ld_q, bt);
   return hipGetLastError();
 }
 

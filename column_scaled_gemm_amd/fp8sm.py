@@ -36,6 +36,13 @@ SIGNATURES = {
     "fp8sm_scaled_mm_ex": (_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _int, _p, _int, _p,
                                   _p, _int, _p]),
     "fp8sm_silu_mul_f32": (_int, [_p, _int, _i64, _i64, _i64, _p, _i64, _p]),
+    "fp8sm_quant_group_batched": (_int, [_p, _int, _i64, _i64, _i64, _i64, _i64, _p, _i32, _u32,
+                                         _int, _int, _p, _i64, _i64, _p, _p]),
+    "fp8sm_quant_static_batched": (_int, [_p, _int, _i64, _i64, _i64, _i64, _i64, _p, _p, _i64,
+                                          _i64, _p]),
+    "fp8sm_scaled_mm_batched": (_int, [_i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64,
+                                       _i64, _i64, _i64, _int, _p, _i64, _int, _p, _i64, _p, _int,
+                                       _p]),
     "fp8sm_scale_bytes": (ctypes.c_size_t, [_int, _int, _i64, _i64, _i32]),
     "fp8sm_status_str": (ctypes.c_char_p, [_int]),
     "fp8sm_force_variant": (_int, [_int]),
@@ -204,9 +211,131 @@ def scaled_mm(a, b, sa, sb, kind_a, kind_b, c=None, M=None, stream=None, bias=No
         return c
     out = {torch.bfloat16: BF16, torch.float16: FP16}[out_dtype]
     if c.dtype != out_dtype or (bias is not None and bias.dtype != out_dtype):
-        raise Fp8smError("fp8sm_scaled_mm_ex: c and bias must have the output dtype")
+        raise TypeError("fp8sm_scaled_mm_ex: c and bias must have the output dtype")
     st = _load().fp8sm_scaled_mm_ex(_ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(c), c.stride(0),
                                     M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb),
                                     None if bias is None else _ptr(bias), out, _stream(stream))
     _check(st, "fp8sm_scaled_mm_ex")
+    return c
+
+
+# ---------------------------------------------------------------- batched calls
+
+def _rows_arg(rows, B):
+    """Device int32 [B] live-row counts, or None."""
+    if rows is None:
+        return None
+    if rows.dtype != torch.int32 or rows.dim() != 1 or rows.numel() != B or not rows.is_cuda:
+        raise ValueError("rows must be a device int32 tensor with one count per batch")
+    return rows
+
+
+def _unit_last(t, what):
+    if t.stride(-1) != 1:
+        raise ValueError(f"{what}: the last dimension must be contiguous")
+
+
+def quant_group_batched(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul=False,
+                        rows=None, q=None, scales=None, stream=None):
+    """x [B, M, K_in] bf16/fp16 with any batch / row strides (unit element
+    stride) -> (codes uint8 [B, M, K_out], scales [B, ...2-D scale shape]).
+    rows: optional device int32 [B] live-row counts (the masked form)."""
+    B, M, K_in = x.shape
+    _unit_last(x, "x")
+    K_out = K_in // 2 if fuse_silu_mul else K_in
+    if group == -1:
+        group = K_out
+    if q is None:
+        q = torch.empty((B, M, K_out), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        dt = torch.uint8 if fmt == SCALE_UE8M0_BYTE else torch.float32
+        scales = torch.empty((B,) + scale_shape(fmt, layout, M, K_out, group), dtype=dt,
+                             device=x.device)
+    _unit_last(q, "q")
+    per = scale_bytes(fmt, layout, M, K_out, group)
+    if not scales.is_contiguous() or scales.numel() * scales.element_size() < B * per:
+        raise ValueError("scales must be contiguous with room for every batch")
+    rows = _rows_arg(rows, B)
+    st = _load().fp8sm_quant_group_batched(
+        _ptr(x), _dtype_code(x), B, M, K_out, x.stride(0) if B > 1 else 0, x.stride(1), _ptr(rows),
+        group, FUSE_SILU_MUL if fuse_silu_mul else 0, fmt, layout, _ptr(q),
+        q.stride(0) if B > 1 else 0, q.stride(1), _ptr(scales), _stream(stream))
+    _check(st, "fp8sm_quant_group_batched")
+    return q, scales
+
+
+def quant_static_batched(x, scale, q=None, stream=None):
+    """x [B, M, K] bf16/fp16 (any batch / row strides) -> codes [B, M, K]."""
+    B, M, K = x.shape
+    _unit_last(x, "x")
+    if q is None:
+        q = torch.empty((B, M, K), dtype=torch.uint8, device=x.device)
+    _unit_last(q, "q")
+    st = _load().fp8sm_quant_static_batched(
+        _ptr(x), _dtype_code(x), B, M, K, x.stride(0) if B > 1 else 0, x.stride(1), _ptr(scale),
+        _ptr(q), q.stride(0) if B > 1 else 0, q.stride(1), _stream(stream))
+    _check(st, "fp8sm_quant_static_batched")
+    return q
+
+
+# rank of one batch's scale operand per kind, and its element count
+_KIND_RANK = {KIND_TENSOR: 0, KIND_ROW: 1, KIND_COL: 1, KIND_GROUP128_UE8M0: 2,
+              KIND_GROUP128_FP32: 2, KIND_BLOCK128: 2}
+
+
+def _scale_batch_stride(t, kind, B, need, what):
+    """0 for a shared scale operand, its leading stride for a per-batch one;
+    checks that every batch's `need` elements exist."""
+    if kind == KIND_TENSOR:
+        if t.numel() == 1:
+            return 0
+        if t.dim() == 1 and t.numel() == B:
+            return t.stride(0)
+        raise ValueError(f"{what}: a TENSOR scale is one element or one per batch")
+    base = _KIND_RANK[kind]
+    if t.dim() == base + 1 and t.shape[0] == B and B > 1:
+        if t[0].numel() < need or not t[0].is_contiguous():
+            raise ValueError(f"{what}: per-batch scales too small or not contiguous")
+        return t.stride(0)
+    if t.numel() < need or not t.is_contiguous():
+        raise ValueError(f"{what}: scales too small or not contiguous")
+    return 0
+
+
+def scaled_mm_batched(a, b, sa, sb, kind_a, kind_b, rows=None, c=None, bias=None,
+                      out_dtype=None, stream=None):
+    """a [B, M, K] uint8 (any batch / row strides); b [N, K] (one weight) or
+    [B, N, K] (one per batch) -> c [B, M, N].  Scales are shared (their 2-D
+    shape) or per batch (a leading B dimension).  rows: optional device int32
+    [B] live-row counts; rows past a batch's count are left as c held them."""
+    B, M, K = a.shape
+    _unit_last(a, "a")
+    _unit_last(b, "b")
+    if b.dim() == 3:
+        if b.shape[0] != B:
+            raise ValueError("a per-batch weight needs one [N, K] slab per batch")
+        N, bs_b = b.shape[1], (b.stride(0) if B > 1 else 0)
+        ldb = b.stride(1)
+    else:
+        N, bs_b, ldb = b.shape[0], 0, b.stride(0)
+    if out_dtype is None:
+        out_dtype = c.dtype if c is not None else torch.bfloat16
+    if c is None:
+        c = torch.empty((B, M, N), dtype=out_dtype, device=a.device)
+    _unit_last(c, "c")
+    if c.dtype != out_dtype or (bias is not None and bias.dtype != out_dtype):
+        raise TypeError("c and bias must have the output dtype")
+    G = (K + 127) // 128
+    need_a = {KIND_TENSOR: 1, KIND_ROW: M, KIND_GROUP128_UE8M0: M * G,
+              KIND_GROUP128_FP32: M * G}[kind_a]
+    need_b = {KIND_TENSOR: 1, KIND_COL: N, KIND_BLOCK128: ((N + 127) // 128) * G}[kind_b]
+    bs_sa = _scale_batch_stride(sa, kind_a, B, need_a, "sa")
+    bs_sb = _scale_batch_stride(sb, kind_b, B, need_b, "sb")
+    out = {torch.bfloat16: BF16, torch.float16: FP16}[out_dtype]
+    rows = _rows_arg(rows, B)
+    st = _load().fp8sm_scaled_mm_batched(
+        B, _ptr(rows), _ptr(a), a.stride(0) if B > 1 else 0, a.stride(1), _ptr(b), bs_b, ldb,
+        _ptr(c), c.stride(0) if B > 1 else 0, c.stride(1), M, N, K, kind_a, _ptr(sa), bs_sa, kind_b,
+        _ptr(sb), bs_sb, None if bias is None else _ptr(bias), out, _stream(stream))
+    _check(st, "fp8sm_scaled_mm_batched")
     return c

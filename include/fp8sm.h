@@ -183,6 +183,64 @@ fp8sm_status fp8sm_scaled_mm_ex(const uint8_t* A, int64_t lda, const uint8_t* B,
                                 hipStream_t stream);
 
 /*
+ * Batched forms.  A batch is nbatch (0..65535) problems of one shape; batch b
+ * reads and writes every operand at that operand's base pointer + b * its
+ * batch stride (strides >= 0, in elements of the operand; a stride of 0
+ * shares the operand between batches).  Two uses from the pages:
+ *  - strided 3-D activations [nbatch, M, K] against one weight ([P2]
+ *    Modifications: the deterministic linear is tested with strided 3-D
+ *    inputs): bs_x / bs_a is the batch stride, ld_x / lda the row stride;
+ *  - the masked per-expert form of the EP-MoE decode path ([P4] commit
+ *    messages and Speed Tests: the fused SiLU-and-mul group quant, masked):
+ *    `rows` is a DEVICE int32 [nbatch] array of live rows per batch (expert);
+ *    batch b processes rows m < clamp(rows[b], 0, M) and leaves the outputs
+ *    of its other rows (codes, scales, C rows) untouched.  NULL: all M rows.
+ *    The counts are read on the device, so the call needs no host sync and
+ *    can be captured in a graph.
+ * Every live row gives bitwise the result the 2-D call gives for that row
+ * with batch b's operands.  Output batch strides must keep batches disjoint
+ * (stride >= (M - 1) * ld + row length when nbatch > 1, else ERR_SHAPE).
+ * Inputs may overlap.  Batch strides obey the alignment of the matching
+ * leading dimension (ERR_ALIGN otherwise); a negative stride or nbatch is
+ * ERR_SHAPE, nbatch > 65535 is ERR_RANGE; rows must be 4-byte aligned.
+ * Other arguments and errors are those of the 2-D call.
+ */
+
+/* fp8sm_quant_group per batch.  x: [nbatch][M][ld_x] with batch stride bs_x
+ * elements; q: batch stride bs_q bytes; scales: nbatch consecutive blocks of
+ * fp8sm_scale_bytes(fmt, lay, M, K_out, group) bytes each (batch-outermost,
+ * so the MN-major layout is [nbatch][G][M_pad], the per-expert column-major
+ * form a grouped GEMM reads). */
+fp8sm_status fp8sm_quant_group_batched(const void* x, fp8sm_dtype in, int64_t nbatch, int64_t M,
+                                       int64_t K_out, int64_t bs_x, int64_t ld_x,
+                                       const int32_t* rows, int32_t group, uint32_t flags,
+                                       fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, uint8_t* q,
+                                       int64_t bs_q, int64_t ld_q, void* scales,
+                                       hipStream_t stream);
+
+/* fp8sm_quant_static per batch, one shared scale (no row counts). */
+fp8sm_status fp8sm_quant_static_batched(const void* x, fp8sm_dtype in, int64_t nbatch, int64_t M,
+                                        int64_t K, int64_t bs_x, int64_t ld_x,
+                                        const float* scale, uint8_t* q, int64_t bs_q,
+                                        int64_t ld_q, hipStream_t stream);
+
+/* fp8sm_scaled_mm_ex per batch.  bs_a, bs_b: bytes (bs_b = 0: one weight for
+ * every batch, the 3-D linear; > 0: one weight per batch, the grouped
+ * per-expert GEMM); bs_c: output elements; bs_sa, bs_sb: elements of the
+ * scale kind's type (bytes for GROUP128_UE8M0, floats otherwise), 0 to share:
+ * a TENSOR scale with stride 1 is one scalar per batch, ROW / COL vectors,
+ * GROUP128 [M][G] and BLOCK128 [NB][KB] arrays repeat per batch.  bias, when
+ * given, is shared.  Dispatch picks the kernel from (M, N, K) as for the 2-D
+ * call. */
+fp8sm_status fp8sm_scaled_mm_batched(int64_t nbatch, const int32_t* rows, const uint8_t* A,
+                                     int64_t bs_a, int64_t lda, const uint8_t* B, int64_t bs_b,
+                                     int64_t ldb, void* C, int64_t bs_c, int64_t ldc, int64_t M,
+                                     int64_t N, int64_t K, fp8sm_scale_kind ka, const void* sa,
+                                     int64_t bs_sa, fp8sm_scale_kind kb, const void* sb,
+                                     int64_t bs_sb, const void* bias, fp8sm_dtype out,
+                                     hipStream_t stream);
+
+/*
  * The fused product alone, in fp32: y[m][k] = RN32(silu(x[m][k]) * x[m][K_out+k])
  * with the same silu as fp8sm_quant_group's FUSE_SILU_MUL ([P4] Modifications
  * 2).  x: device bf16/fp16 [M][ld_x], ld_x >= 2*K_out; y: device fp32

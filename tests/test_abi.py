@@ -120,6 +120,64 @@ def test_quant_group_rejects_bad_arguments():
     assert q(M=0) == E["OK"]
 
 
+def test_batched_calls_reject_bad_batches_before_any_launch():
+    from column_scaled_gemm_amd import fp8sm
+    lib = fp8sm.lib()
+    E = {v: k for k, v in fp8sm.STATUS.items()}
+    P = ctypes.c_void_p
+
+    def qb(**kw):
+        a = dict(x=16, B=3, M=4, K=256, bsx=2048, ldx=256, rows=0, group=128, q=16, bsq=1024,
+                 ldq=256, s=16)
+        a.update(kw)
+        return lib.fp8sm_quant_group_batched(P(a["x"]), 0, a["B"], a["M"], a["K"], a["bsx"],
+                                             a["ldx"], P(a["rows"]), a["group"], 0, 0, 0,
+                                             P(a["q"]), a["bsq"], a["ldq"], P(a["s"]), P(0))
+    assert qb(B=-1) == E["ERR_SHAPE"]
+    assert qb(B=65536) == E["ERR_RANGE"]
+    assert qb(bsx=-8) == E["ERR_SHAPE"]
+    assert qb(bsx=2052) == E["ERR_ALIGN"]                    # batch stride of x % 8
+    assert qb(bsq=1020) == E["ERR_ALIGN"]
+    assert qb(bsq=1016) == E["ERR_SHAPE"]                    # batches of q would overlap
+    assert qb(rows=18) == E["ERR_ALIGN"]                     # int32 counts
+    assert qb(B=0) == E["OK"] and qb(M=0) == E["OK"]
+    assert qb(x=0) == E["ERR_NULL"]
+
+    def sb(**kw):
+        a = dict(x=16, B=2, M=4, K=64, bsx=256, ldx=64, s=16, q=16, bsq=256, ldq=64)
+        a.update(kw)
+        return lib.fp8sm_quant_static_batched(P(a["x"]), 0, a["B"], a["M"], a["K"], a["bsx"],
+                                              a["ldx"], P(a["s"]), P(a["q"]), a["bsq"], a["ldq"],
+                                              P(0))
+    assert sb(bsq=248) == E["ERR_SHAPE"]
+    assert sb(bsx=-8) == E["ERR_SHAPE"]
+    assert sb(bsx=12) == E["ERR_ALIGN"]
+    assert sb(B=70000) == E["ERR_RANGE"]
+    assert sb(q=0) == E["ERR_NULL"]
+
+    def mb(**kw):
+        a = dict(B=4, rows=0, A=16, bsa=64 * 512, lda=512, Bp=16, bsb=0, ldb=512, C=16,
+                 bsc=64 * 256, ldc=256, M=64, N=256, K=512, ka=1, sa=16, bssa=64, kb=2, sb=16,
+                 bssb=0, bias=0, out=0)
+        a.update(kw)
+        return lib.fp8sm_scaled_mm_batched(a["B"], P(a["rows"]), P(a["A"]), a["bsa"], a["lda"],
+                                           P(a["Bp"]), a["bsb"], a["ldb"], P(a["C"]), a["bsc"],
+                                           a["ldc"], a["M"], a["N"], a["K"], a["ka"], P(a["sa"]),
+                                           a["bssa"], a["kb"], P(a["sb"]), a["bssb"], P(a["bias"]),
+                                           a["out"], P(0))
+    assert mb(B=-2) == E["ERR_SHAPE"]
+    assert mb(B=65536) == E["ERR_RANGE"]
+    assert mb(bsa=8) == E["ERR_ALIGN"]                       # fp8 rows stay 16-byte aligned
+    assert mb(bsb=24) == E["ERR_ALIGN"]
+    assert mb(bsc=12) == E["ERR_ALIGN"]
+    assert mb(bsc=64 * 256 - 8) == E["ERR_SHAPE"]            # C batches would overlap
+    assert mb(bssa=-1) == E["ERR_SHAPE"]
+    assert mb(rows=2) == E["ERR_ALIGN"]
+    assert mb(ka=3, kb=5, out=1) == E["ERR_UNSUPPORTED"]     # blockwise: bf16 only
+    assert mb(B=0) == E["OK"]
+    assert mb(A=0) == E["ERR_NULL"]
+
+
 def test_variant_table_routes_decode_shapes_by_m():
     from column_scaled_gemm_amd import fp8sm
     assert fp8sm.variant_count() >= 3
