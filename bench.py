@@ -33,8 +33,8 @@ PEAK_HBM = 8000.0           # GB/s
 # passes, scaled by a plain-copy calibration (profiles/
 # gemm_rowwise_128x256_qkv_traffic.md).  Valid only for the gemm.hip source it
 # was measured on; reported as null once that file changes.
-TRAFFIC = {"gemm_src_sha256_prefix": "1d3ddf8fb09c4bef", "workload": "qkv",
-           "kernel": "tile128x256", "bytes": 2187.2e6 + 358.2e6}
+TRAFFIC = {"gemm_src_sha256_prefix": "c07e600d00896c6f", "workload": "qkv",
+           "kernel": "tile128x256", "bytes": 2187.7e6 + 358.1e6}
 
 
 def measured_traffic(workload, variant):
@@ -261,6 +261,52 @@ def suite(reps):
              TFLOPs=round(tf, 1), bf16_peak_frac=round(tf / PEAK_BF16_MFMA, 4), cache="warm")
         del qa, ea, c
         torch.cuda.empty_cache()
+
+    # f2: masked EP-MoE decode -- fused SiLU-and-mul + 1x128 UE8M0 quant of the
+    # live rows of each expert's slab, then the grouped blockwise down GEMM
+    mo = inputs.masked_moe()
+    E, Tm, H, I = inputs.MOE_E, inputs.MOE_T, inputs.MOE_HIDDEN, inputs.MOE_INTER
+    rows = torch.from_numpy(mo.rows).to(dev)
+    live, active = int(mo.rows.sum()), int((mo.rows > 0).sum())
+    nrot = _rotations(2 * E * Tm * 2 * I, True)
+    gus = [mo.gu.to(dev) for _ in range(nrot)]
+    q = torch.empty((E, Tm, I), dtype=torch.uint8, device=dev)
+    es = torch.empty((E, Tm, I // 128), dtype=torch.uint8, device=dev)
+    us_m, hb = _time_launches(
+        lambda i: fp8sm.quant_group_batched(gus[i % nrot], 128, fp8sm.SCALE_UE8M0_BYTE,
+                                            fuse_silu_mul=True, rows=rows, q=q, scales=es,
+                                            stream=stream), max(reps, nrot), nrot, stream)
+    mbytes = live * (4 * I + I + I // 128)
+    emit("f2 masked fused SiLU-mul + 1x128 UE8M0 quant",
+         workload=f"bf16[{E},{Tm},{2 * I}] {live} live rows", us=round(us_m, 2),
+         GBps=round(mbytes / us_m / 1e3, 1), hbm_frac=round(mbytes / us_m / 1e3 / PEAK_HBM, 3),
+         cache="cold", host_bound=hb)
+    del gus
+    nrot = _rotations(E * H * I, True)
+    wqs, wss = [], []
+    for _ in range(nrot):
+        wq = torch.empty((E, H, I), dtype=torch.uint8, device=dev)
+        ws = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=dev)
+        for e in range(E):
+            fp8sm.quant_weight_block128(mo.w[e].to(dev), q=wq[e], scales=ws[e])
+        wqs.append(wq)
+        wss.append(ws)
+    del mo
+    c = torch.empty((E, Tm, H), dtype=torch.bfloat16, device=dev)
+    us_e, hb = _time_launches(
+        lambda i: fp8sm.scaled_mm_batched(q, wqs[i % nrot], es, wss[i % nrot],
+                                          fp8sm.KIND_GROUP128_UE8M0, fp8sm.KIND_BLOCK128,
+                                          rows=rows, c=c, stream=stream),
+        max(reps, nrot), nrot, stream)
+    ebytes = (active * H * I + live * (I + I // 128) + active * (H // 128) * (I // 128) * 4
+              + live * H * 2)
+    emit("f2 masked grouped blockwise GEMM",
+         workload=f"{E} experts x {Tm}-row slabs, {live} live rows, K={I} N={H}",
+         us=round(us_e, 1), GBps=round(ebytes / us_e / 1e3, 1),
+         hbm_frac=round(ebytes / us_e / 1e3 / PEAK_HBM, 3),
+         TFLOPs=round(2.0 * live * H * I / us_e / 1e6, 1), cache="cold", host_bound=hb)
+    del wqs, wss, q, es, c
+    torch.cuda.empty_cache()
     return out
 
 

@@ -30,6 +30,15 @@ fused       gate|up [4096, 2 x 7168] N(0,1); a seeded Bernoulli(0.05) choice of
             subnormal on purpose); rows with r % 512 == 7 are all zero.
             Returned in bf16 and in fp16 from the same draws.  W [4096, 7168]
             N(0, 0.02) for the blockwise GEMM.
+masked_moe  the masked EP-MoE decode step of sglang PR #33533 (Speed Tests:
+            graph-captured decode, bf16, group 128, UE8M0, fused SiLU-and-mul,
+            masked), whose shapes the pages do not print.  Stand-in: 32 local
+            experts (256 routed experts over 8 ranks), each with a 128-row
+            slab; live rows per expert ~ Poisson(32) clamped to the slab (a
+            decode batch of 128 tokens per rank, top-8 routing); gate|up
+            [32, 128, 2 x 2048] N(0,1) (all slab rows drawn, dead ones
+            included); down-projection weights [32, 7168, 2048] N(0, 0.02),
+            hidden 7168 as in the fused workload.
 """
 from dataclasses import dataclass, field
 from typing import Dict, Optional
@@ -52,6 +61,7 @@ DECODE_NS = (4096, 14336)
 DECODE_MS = (1, 4, 16)
 FUSED_M, FUSED_K, FUSED_N = 4096, 7168, 4096
 FUSED_GROUP = 128
+MOE_E, MOE_T, MOE_HIDDEN, MOE_INTER, MOE_MEAN_ROWS = 32, 128, 7168, 2048, 32
 
 
 def rng(seed=SEED):
@@ -141,6 +151,24 @@ def fused(M=FUSED_M, K=FUSED_K, N=FUSED_N, seed=SEED) -> FusedInputs:
     w = r.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
     return FusedInputs(to_dtype(gu, torch.bfloat16), to_dtype(gu, torch.float16),
                        to_dtype(w, torch.bfloat16), tiny, zero_rows)
+
+
+@dataclass
+class MaskedMoEInputs:
+    gu: torch.Tensor                   # [E, T, 2 * inter] bf16 gate | up
+    rows: np.ndarray                   # int32 [E] live rows per expert
+    w: torch.Tensor                    # [E, hidden, inter] bf16
+
+
+def masked_moe(E=MOE_E, T=MOE_T, hidden=MOE_HIDDEN, inter=MOE_INTER, mean_rows=MOE_MEAN_ROWS,
+               seed=SEED) -> MaskedMoEInputs:
+    r = rng(seed)
+    rows = np.minimum(r.poisson(mean_rows, E), T).astype(np.int32)
+    gu = r.standard_normal((E, T, 2 * inter), dtype=np.float32)
+    w = np.empty((E, hidden, inter), dtype=np.float32)
+    for e in range(E):                 # one expert at a time bounds the fp32 peak
+        w[e] = r.standard_normal((hidden, inter), dtype=np.float32) * np.float32(0.02)
+    return MaskedMoEInputs(to_dtype(gu), rows, to_dtype(w))
 
 
 def random_codes(shape, seed=SEED) -> np.ndarray:
