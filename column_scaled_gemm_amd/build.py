@@ -27,6 +27,7 @@ FLAGS = [
     "-ffp-contract=off",
     "-Wall",
     "-I", os.path.join(ROOT, "include"),
+    "-I", BUILD,          # silu_tables.inc, generated below
 ]
 
 
@@ -53,8 +54,24 @@ def _compile(src, obj, verbose):
     return obj
 
 
+def _gen_silu_tables():
+    """Compile and run the host generator of the constant SiLU tables."""
+    exe = os.path.join(BUILD, "gen_silu_tables")
+    cmd = [shutil.which("g++") or "g++", "-std=c++17", "-O2", "-ffp-contract=off",
+           "-fno-fast-math", os.path.join(CSRC, "gen_silu_tables.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("gen_silu_tables build failed:\n" + r.stdout + r.stderr)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("gen_silu_tables failed:\n" + r.stderr)
+    with open(os.path.join(BUILD, "silu_tables.inc"), "w") as f:
+        f.write(r.stdout)
+
+
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
+    _gen_silu_tables()
     objs = [os.path.join(BUILD, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         list(ex.map(lambda p: _compile(p[0], p[1], verbose), zip(SOURCES, objs)))

@@ -36,15 +36,6 @@ __device__ __forceinline__ void widen8(const uint4 v, float* f) {
   }
 }
 
-// silu(g) = RN32(g / RN32(1 + E)), E the correctly rounded fp32 e^-g.  E is
-// evaluated as the fp64 exponential rounded to fp32; the parity tests check
-// exhaustively that this is the correctly rounded value for every gate value
-// a bf16 or fp16 input can hold.  The divide is the IEEE fp32 divide.
-__device__ __forceinline__ float silu_f32(float g) {
-  const float e = (float)exp(-(double)g);
-  const float d = 1.0f + e;
-  return g / d;
-}
 
 // Clamp to the E4M3FN range and convert eight fp32 values to codes
 // (round to nearest even, sign of zero kept).  The hardware conversion does

@@ -1,9 +1,12 @@
 // SiLU of a bf16 / fp16 gate through an LDS table (gfx950).
 //
 // silu(g) = RN32(g / RN32(1 + RN32(e^-g))) depends only on the gate, and a
-// gate held in bf16 or fp16 takes one of 65536 values, so a workgroup builds
-// a table once and each element costs a lookup instead of an fp64
-// exponential and an IEEE divide.  Tables are indexed by the sign and the
+// gate held in bf16 or fp16 takes one of 65536 values, so each element costs
+// a table lookup instead of an fp64 exponential and an IEEE divide.  The
+// tables are constant data of the code object, computed on the host at build
+// time by gen_silu_tables.cpp with the formulas below; a workgroup copies its
+// table from global memory (L2-resident after the first workgroups) into LDS
+// with 16-byte loads.  Tables are indexed by the sign and the
 // fp32 exponent field E of g, clamped to a window; outside 2^-26 <= |g| < 2^7
 // (E = 101..133) the value has a closed form:
 //  * |g| < 2^-26: RN32(e^-g) = 1, so silu = g / 2 (exact).
@@ -32,6 +35,18 @@
 
 namespace fp8sm {
 
+#include "silu_tables.inc"  // kSiluBf16Table, kSiluF16Table (generated)
+
+// Every thread of the workgroup calls this; the caller places a barrier
+// before the first lookup.
+template <int BYTES>
+__device__ __forceinline__ void copy_table(void* lds, const void* src, int tid, int nthr) {
+  static_assert(BYTES % 16 == 0, "16-byte chunks");
+  const uint4* s = static_cast<const uint4*>(src);
+  uint4* d = static_cast<uint4*>(lds);
+  for (int j = tid; j < BYTES / 16; j += nthr) d[j] = s[j];
+}
+
 template <bool F16>
 struct SiluTable;
 
@@ -40,21 +55,10 @@ struct SiluTable<false> {
   static constexpr uint32_t kE0 = 100, kRows = 35;  // E = 100 .. 134
   static constexpr int kBytes = 2 * kRows * 128 * 8;
 
-  // Every thread of the workgroup calls build(); the caller places a barrier
-  // before the first lookup.
+  static_assert(sizeof(kSiluBf16Table) == kBytes, "generated bf16 table size");
+
   __device__ static void build(void* lds, int tid, int nthr) {
-    float2* t = static_cast<float2*>(lds);
-    for (int j = tid; j < (int)(2 * kRows * 128); j += nthr) {
-      const uint32_t s = j / (kRows * 128), r = (j / 128) % kRows, m = j % 128;
-      float2 v;
-      if (r == 0)
-        v = make_float2(0.5f, -0.0f);
-      else if (r == kRows - 1)
-        v = make_float2(s ? 0.0f : 1.0f, -0.0f);
-      else
-        v = make_float2(0.0f, silu_f32(__uint_as_float(s << 31 | (r + kE0) << 23 | m << 16)));
-      t[j] = v;
-    }
+    copy_table<kBytes>(lds, kSiluBf16Table, tid, nthr);
   }
 
   __device__ static float lookup(const void* lds, float g) {
@@ -81,20 +85,10 @@ struct SiluTable<true> {
   static constexpr int kHalf = 2 * kRows * 32;      // entries per factor table
   static constexpr int kBytes = 2 * kHalf * 8;
 
+  static_assert(sizeof(kSiluF16Table) == kBytes, "generated fp16 table size");
+
   __device__ static void build(void* lds, int tid, int nthr) {
-    double* h = static_cast<double*>(lds);
-    double* l = h + kHalf;
-    for (int j = tid; j < kHalf; j += nthr) {
-      const uint32_t s = j / (kRows * 32), r = (j / 32) % kRows, m = j % 32;
-      if (r == kRows - 1) {
-        h[j] = s ? __builtin_inf() : 0.0;
-        l[j] = 1.0;
-      } else {
-        h[j] = exp(-(double)__uint_as_float(s << 31 | (r + kE0) << 23 | m << 18));
-        const double gl = ldexp((double)m, (int)(r + kE0) - 137);  // m * 2^(E-127-10)
-        l[j] = exp(s ? gl : -gl);
-      }
-    }
+    copy_table<kBytes>(lds, kSiluF16Table, tid, nthr);
   }
 
   __device__ static float lookup(const void* lds, float g) {
