@@ -299,6 +299,31 @@ def test_blockwise_fp32_group_scales_ragged():
     assert_within_tolerance(bf16_bits(c), og.blockwise_mm(A, sa, B, sb), K, "blockwise fp32 ragged")
 
 
+@pytest.mark.parametrize("shape", [(70, 264, 400), (5, 136, 1040), (33, 128, 128),
+                                   (130, 520, 2064), (32, 384, 7168)])
+def test_blockwise_ue8m0_ragged_and_row_invariant(shape):
+    # ragged M / N / K (partial K blocks) against the oracle, and a row's bits
+    # do not depend on M
+    M, N, K = shape
+    print(f"[case] blockwise ue8m0 M={M} N={N} K={K}", flush=True)
+    r = inputs.rng(M + N + K)
+    G = (K + 127) // 128
+    A = inputs.random_codes((M, K), seed=M)
+    B = inputs.random_codes((N, K), seed=N)
+    e = r.integers(119, 131, size=(M, G)).astype(np.uint8)
+    sb = np.exp2(r.uniform(-14, -6, ((N + 127) // 128, G))).astype(F32)
+
+    def run(rows):
+        c = fp8sm.scaled_mm(to_gpu_u8(A[:rows]), to_gpu_u8(B), torch.from_numpy(e[:rows]).to(cuda()),
+                            to_gpu_f32(sb), fp8sm.KIND_GROUP128_UE8M0, fp8sm.KIND_BLOCK128)
+        torch.cuda.synchronize()
+        return bf16_bits(c)
+    full = run(M)
+    assert np.array_equal(run(min(M, 5)), full[:5])
+    a_vals = np.exp2(e.astype(np.float64) - 127).astype(F32)
+    assert_within_tolerance(full, og.blockwise_mm(A, a_vals, B, sb), K, f"ue8m0 {shape}")
+
+
 def test_k_zero_writes_zeros():
     c = torch.full((5, 16), 7.0, dtype=torch.bfloat16, device=cuda())
     a = torch.zeros((5, 16), dtype=torch.uint8, device=cuda())
