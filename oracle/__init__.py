@@ -26,6 +26,11 @@ title and section):
                key source excerpts).
 * ``bf16``   -- round-to-nearest-even from float64 to bfloat16.
 * ``fp16``   -- round-to-nearest-even from float64 to IEEE half.
+* ``weights`` -- load-time preparation of a fused per-tensor weight:
+               requantization of every logical partition to the largest
+               partition scale, and the per-partition scalar broadcast to
+               per-channel scales (prhub digest of PR #33148, key source
+               excerpts).
 * ``batched`` -- the batched / masked forms: each batch's live rows (a
                per-batch count, clamped to the slab) go through the 2-D
                definitions with that batch's operands (PR #33533 commit
