@@ -307,6 +307,27 @@ def suite(reps):
          TFLOPs=round(2.0 * live * H * I / us_e / 1e6, 1), cache="cold", host_bound=hb)
     del wqs, wss, q, es, c
     torch.cuda.empty_cache()
+
+    # f4: load-time requantization of the fused QKV weight to its largest
+    # partition scale (partition widths 16384 / 2560 / 2560 rows: a stand-in,
+    # the pages print none), then the per-channel broadcast
+    Nq, Kq = inputs.ROWWISE_SHAPES["qkv"][1], inputs.ROWWISE_SHAPES["qkv"][2]
+    widths = [16384, 2560, 2560]
+    nrot = _rotations(2 * Nq * Kq, True)
+    wcs = [torch.from_numpy(inputs.random_codes((Nq, Kq), seed=40 + i)).to(dev)
+           for i in range(nrot)]
+    ps = torch.tensor([0.011, 0.017, 0.013], dtype=torch.float32, device=dev)
+    wq = torch.empty((Nq, Kq), dtype=torch.uint8, device=dev)
+    ms = torch.empty(1, dtype=torch.float32, device=dev)
+    us_r, hb = _time_launches(
+        lambda i: fp8sm.requantize_max_scale(wcs[i % nrot], ps, widths, q=wq, max_scale=ms,
+                                             stream=stream), max(reps, nrot), nrot, stream)
+    rbytes = 2 * Nq * Kq
+    emit("f4 requantize fused weight to the max scale", workload=f"qkv weight [{Nq},{Kq}], 3 partitions",
+         us=round(us_r, 1), GBps=round(rbytes / us_r / 1e3, 1),
+         hbm_frac=round(rbytes / us_r / 1e3 / PEAK_HBM, 3), cache="cold", host_bound=hb)
+    del wcs, wq
+    torch.cuda.empty_cache()
     return out
 
 

@@ -212,6 +212,57 @@ fp8sm_status fp8sm_quant_weight_block128(const void* w, fp8sm_dtype in, int64_t 
   return launched(launch_quant_wblock(w, in == FP8SM_FP16, N, K, ld_w, q, ld_q, scales, stream));
 }
 
+// Partition offsets from host widths: 1..16 non-negative widths summing to N.
+static fp8sm_status weight_parts(const int64_t* widths, int32_t nparts, int64_t N,
+                                 WeightParts* parts) {
+  if (!widths) return FP8SM_ERR_NULL;
+  if (nparts < 1 || nparts > kMaxWeightParts) return FP8SM_ERR_RANGE;
+  parts->n = nparts;
+  parts->off[0] = 0;
+  for (int i = 0; i < nparts; ++i) {
+    if (widths[i] < 0) return FP8SM_ERR_SHAPE;
+    parts->off[i + 1] = parts->off[i] + widths[i];
+    if (parts->off[i + 1] > kMaxDim) return FP8SM_ERR_RANGE;
+  }
+  if (N >= 0 && parts->off[nparts] != N) return FP8SM_ERR_SHAPE;
+  return FP8SM_OK;
+}
+
+fp8sm_status fp8sm_requantize_max_scale(const uint8_t* w, int64_t ldw, int64_t N, int64_t K,
+                                        const int64_t* widths, int32_t nparts,
+                                        const float* scales, uint8_t* q, int64_t ldq,
+                                        float* max_scale, hipStream_t stream) {
+  if (N < 0 || K < 0) return FP8SM_ERR_SHAPE;
+  if (N > kMaxDim || K > kMaxDim) return FP8SM_ERR_RANGE;
+  WeightParts parts;
+  fp8sm_status st = weight_parts(widths, nparts, N, &parts);
+  if (st != FP8SM_OK) return st;
+  if (ldw < K || ldq < K) return FP8SM_ERR_SHAPE;
+  if (K % 16 || ldw % 16 || ldq % 16) return FP8SM_ERR_ALIGN;
+  if (q == w && ldq != ldw) return FP8SM_ERR_SHAPE;  // in place only row for row
+  if (!scales || !max_scale) return FP8SM_ERR_NULL;
+  if (!aligned(scales, 4) || !aligned(max_scale, 4)) return FP8SM_ERR_ALIGN;
+  if ((N > 0 && K > 0) && (!w || !q)) return FP8SM_ERR_NULL;
+  if ((w && !aligned(w, 16)) || (q && !aligned(q, 16))) return FP8SM_ERR_ALIGN;
+  st = check_device();
+  if (st != FP8SM_OK) return st;
+  return launched(launch_requant_max(w, ldw, N, K, parts, scales, q, ldq, max_scale, stream));
+}
+
+fp8sm_status fp8sm_scales_to_channelwise(const float* scales, const int64_t* widths,
+                                         int32_t nparts, float* out, hipStream_t stream) {
+  WeightParts parts;
+  fp8sm_status st = weight_parts(widths, nparts, -1, &parts);
+  if (st != FP8SM_OK) return st;
+  const int64_t N = parts.off[nparts];
+  if (N == 0) return FP8SM_OK;
+  if (!scales || !out) return FP8SM_ERR_NULL;
+  if (!aligned(scales, 4) || !aligned(out, 4)) return FP8SM_ERR_ALIGN;
+  st = check_device();
+  if (st != FP8SM_OK) return st;
+  return launched(launch_channelwise(scales, parts, N, out, stream));
+}
+
 fp8sm_status fp8sm_silu_mul_f32(const void* x, fp8sm_dtype in, int64_t M, int64_t K_out,
                                 int64_t ld_x, float* y, int64_t ld_y, hipStream_t stream) {
   if (in != FP8SM_BF16 && in != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;

@@ -52,6 +52,19 @@ hipError_t launch_silu_mul(const void* x, bool f16, int64_t M, int64_t K, int64_
 hipError_t launch_quant_wblock(const void* w, bool f16, int64_t N, int64_t K, int64_t ld_w,
                                uint8_t* q, int64_t ld_q, float* scales, hipStream_t s);
 
+// Logical partitions of a fused weight's rows: partition i is rows
+// off[i] .. off[i + 1] - 1 (off[0] = 0, off[n] = N).
+constexpr int kMaxWeightParts = 16;
+struct WeightParts {
+  int64_t off[kMaxWeightParts + 1];
+  int n;
+};
+hipError_t launch_requant_max(const uint8_t* w, int64_t ldw, int64_t N, int64_t K,
+                              const WeightParts& parts, const float* scales, uint8_t* q,
+                              int64_t ldq, float* max_out, hipStream_t s);
+hipError_t launch_channelwise(const float* scales, const WeightParts& parts, int64_t N, float* out,
+                              hipStream_t s);
+
 struct GemmArgs {
   const uint8_t* A;
   int64_t lda;

@@ -194,7 +194,9 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
     int64_t mpad, QuantBatch bt) {
   __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
   M = (int)enter_batch<FMT>(bt, x, q, scales, M);
-  if (M == 0) return;  // the whole workgroup: M is uniform
+  // a workgroup whose first group is past the batch's groups has no work at
+  // any step: it leaves before copying the table (uniform, before the barrier)
+  if ((int64_t)blockIdx.x * 256 >= (int64_t)M * G) return;
   const int lane = threadIdx.x & 63;
   const int quarter = lane >> 4;
   const int l16 = lane & 15;
@@ -203,13 +205,30 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
   // nw apart, i.e. each cursor moves by 16 nw groups = (drow, dgrp)
   const int64_t nw = (int64_t)gridDim.x * 16;
   int64_t w = (int64_t)blockIdx.x * 16 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int drow = (int)(nw * 16 / G), dgrp = (int)(nw * 16 - (int64_t)drow * G);
+  int drow, dgrp;
   int cr[kQuads], cc[kQuads];
+  if constexpr (O32) {
+    // M * G < 2^23 here (the host checked every byte offset against 2^32),
+    // and w * 16 < 256 * gridDim.x: 32-bit divisions are exact and far
+    // cheaper than 64-bit ones
+    const uint32_t ug = (uint32_t)G, step = (uint32_t)nw * 16u;
+    drow = (int)(step / ug);
+    dgrp = (int)(step - (uint32_t)drow * ug);
 #pragma unroll
-  for (int u = 0; u < kQuads; ++u) {
-    const int64_t gid = w * 16 + 4 * u + quarter;
-    cr[u] = (int)(gid / G);
-    cc[u] = (int)(gid - (int64_t)cr[u] * G);
+    for (int u = 0; u < kQuads; ++u) {
+      const uint32_t gid = (uint32_t)w * 16u + 4u * u + (uint32_t)quarter;
+      cr[u] = (int)(gid / ug);
+      cc[u] = (int)(gid - (uint32_t)cr[u] * ug);
+    }
+  } else {
+    drow = (int)(nw * 16 / G);
+    dgrp = (int)(nw * 16 - (int64_t)drow * G);
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+      const int64_t gid = w * 16 + 4 * u + quarter;
+      cr[u] = (int)(gid / G);
+      cc[u] = (int)(gid - (int64_t)cr[u] * G);
+    }
   }
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
   auto fetch = [&](G128Step& st) {
@@ -475,7 +494,7 @@ __global__ __launch_bounds__(1024) void quant_token_fused_kernel(
     uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scales, QuantBatch bt) {
   __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
   M = enter_batch<FMT>(bt, x, q, scales, M);
-  if (M == 0) return;  // the whole workgroup: M is uniform
+  if ((int64_t)blockIdx.x * 16 >= M) return;  // no row for any wavefront (uniform)
   SiluTable<F16>::build(tab, threadIdx.x, 1024);
   __syncthreads();
   for (int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6); row < M;
@@ -585,6 +604,66 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Load-time requantization of a fused per-tensor weight (the weight loading of
+// the prhub digest of sglang PR #33148, key source excerpts): the rows of
+// logical partition i (offsets in `parts`) hold codes quantized with scale
+// s_i; every code is decoded exactly, scaled back in fp32 and quantized again
+// against s_max = max_i s_i with the static rule:
+//   q' = E4M3(clamp(RN32(RN32(dec(q) * s_i) * RN32(1 / s_max))))
+// Each thread converts one 16-byte chunk (16 codes) of the flattened
+// (row, chunk) space; reading and writing the same chunk makes q == w safe.
+__global__ __launch_bounds__(256) void requant_max_kernel(
+    const uint8_t* w, int64_t ldw, int64_t N, int64_t K, WeightParts parts,
+    const float* __restrict__ scales, uint8_t* q, int64_t ldq, float* __restrict__ max_out) {
+  float smax = scales[0];
+  for (int i = 1; i < parts.n; ++i) smax = fmaxf(smax, scales[i]);
+  const float inv = 1.0f / smax;
+  if (blockIdx.x == 0 && threadIdx.x == 0) max_out[0] = smax;
+  const int64_t nch = K >> 4;
+  const int64_t total = N * nch;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / nch, c = idx - r * nch;
+    int part = 0;
+    while (part + 1 < parts.n && r >= parts.off[part + 1]) ++part;
+    const float si = scales[part];
+    const uint4 v = *reinterpret_cast<const uint4*>(w + r * ldw + c * 16);
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float y[8];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int word = (int)wd[2 * h + k];
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);  // bytes 0, 1 (exact)
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);   // bytes 2, 3
+        y[4 * k] = (lo[0] * si) * inv;
+        y[4 * k + 1] = (lo[1] * si) * inv;
+        y[4 * k + 2] = (hi[0] * si) * inv;
+        y[4 * k + 3] = (hi[1] * si) * inv;
+      }
+      const uint2 e = to_e4m3_x8(y);
+      o[2 * h] = e.x;
+      o[2 * h + 1] = e.y;
+    }
+    *reinterpret_cast<uint4*>(q + r * ldq + c * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Per-partition scalar scales broadcast to the output channels.
+__global__ __launch_bounds__(256) void channelwise_kernel(const float* __restrict__ scales,
+                                                          WeightParts parts, int64_t N,
+                                                          float* __restrict__ out) {
+  for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < N;
+       n += (int64_t)gridDim.x * blockDim.x) {
+    int part = 0;
+    while (part + 1 < parts.n && n >= parts.off[part + 1]) ++part;
+    out[n] = scales[part];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host-side launchers
 
 // Runs f(std::integral_constant<int, FMT>) for the runtime scale format.
@@ -647,8 +726,10 @@ static hipError_t launch_g128_fused(int fmt, const QuantArgs& a, hipStream_t s) 
   const unsigned blocks = persistent_blocks(16 * 16, a.M * G, a.batch.count);  // 16 waves x 16 groups
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   // every byte offset the kernel forms below 2^32: 32-bit address arithmetic
+  // (bf16 only: the fp16 form, whose lookup holds fp64 temporaries, spills at
+  // its 128-register budget with it and runs faster without)
   const uint64_t lim = (uint64_t)1 << 32;
-  const bool o32 = (uint64_t)a.M * (uint64_t)a.ld_x * 2 + 2 * (uint64_t)a.K < lim &&
+  const bool o32 = !F16 && (uint64_t)a.M * (uint64_t)a.ld_x * 2 + 2 * (uint64_t)a.K < lim &&
                    (uint64_t)a.M * (uint64_t)a.ld_q < lim &&
                    (uint64_t)(a.mn_major ? G * a.mpad : a.M * G) < lim;
   return with_fmt(fmt, [&](auto f) {
@@ -784,6 +865,25 @@ hipError_t launch_silu_mul(const void* x, bool f16, int64_t M, int64_t K, int64_
   else
     hipLaunchKernelGGL((silu_mul_kernel<false>), dim3(blocks), dim3(1024), 0, s, xx, M, K, ld_x,
                        y, ld_y);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_max(const uint8_t* w, int64_t ldw, int64_t N, int64_t K,
+                              const WeightParts& parts, const float* scales, uint8_t* q,
+                              int64_t ldq, float* max_out, hipStream_t s) {
+  const int64_t chunks = N * (K / 16);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((chunks + 255) / 256, 65536));
+  hipLaunchKernelGGL(requant_max_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, ldw, N, K,
+                     parts, scales, q, ldq, max_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_channelwise(const float* scales, const WeightParts& parts, int64_t N, float* out,
+                              hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((N + 255) / 256, 65536);
+  hipLaunchKernelGGL(channelwise_kernel, dim3((unsigned)blocks), dim3(256), 0, s, scales, parts, N,
+                     out);
   return hipGetLastError();
 }
 

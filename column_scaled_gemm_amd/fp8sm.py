@@ -36,6 +36,8 @@ SIGNATURES = {
     "fp8sm_scaled_mm_ex": (_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _int, _p, _int, _p,
                                   _p, _int, _p]),
     "fp8sm_silu_mul_f32": (_int, [_p, _int, _i64, _i64, _i64, _p, _i64, _p]),
+    "fp8sm_requantize_max_scale": (_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _p, _i64, _p, _p]),
+    "fp8sm_scales_to_channelwise": (_int, [_p, _p, _i32, _p, _p]),
     "fp8sm_quant_group_batched": (_int, [_p, _int, _i64, _i64, _i64, _i64, _i64, _p, _i32, _u32,
                                          _int, _int, _p, _i64, _i64, _p, _p]),
     "fp8sm_quant_static_batched": (_int, [_p, _int, _i64, _i64, _i64, _i64, _i64, _p, _p, _i64,
@@ -339,3 +341,38 @@ def scaled_mm_batched(a, b, sa, sb, kind_a, kind_b, rows=None, c=None, bias=None
         _ptr(sb), bs_sb, None if bias is None else _ptr(bias), out, _stream(stream))
     _check(st, "fp8sm_scaled_mm_batched")
     return c
+
+
+# ---------------------------------------------------------------- weight preparation
+
+def _widths_arg(widths):
+    arr = (ctypes.c_int64 * len(widths))(*[int(v) for v in widths])
+    return arr, len(widths)
+
+
+def requantize_max_scale(w, scales, widths, q=None, max_scale=None, stream=None):
+    """w uint8 [N, K] fused weight codes, scales fp32 device [P], widths: host
+    list of P row counts -> (max_scale fp32 [1], codes requantized to it).
+    Pass q=w to convert in place."""
+    N, K = w.shape
+    _unit_last(w, "w")
+    if q is None:
+        q = torch.empty_like(w)
+    if max_scale is None:
+        max_scale = torch.empty(1, dtype=torch.float32, device=w.device)
+    arr, n = _widths_arg(widths)
+    st = _load().fp8sm_requantize_max_scale(_ptr(w), w.stride(0), N, K, arr, n, _ptr(scales),
+                                            _ptr(q), q.stride(0), _ptr(max_scale),
+                                            _stream(stream))
+    _check(st, "fp8sm_requantize_max_scale")
+    return max_scale, q
+
+
+def scales_to_channelwise(scales, widths, out=None, stream=None):
+    """Device fp32 [P] per-partition scalars -> fp32 [sum(widths)] per channel."""
+    arr, n = _widths_arg(widths)
+    if out is None:
+        out = torch.empty(int(sum(widths)), dtype=torch.float32, device=scales.device)
+    st = _load().fp8sm_scales_to_channelwise(_ptr(scales), arr, n, _ptr(out), _stream(stream))
+    _check(st, "fp8sm_scales_to_channelwise")
+    return out

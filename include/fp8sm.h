@@ -241,6 +241,40 @@ fp8sm_status fp8sm_scaled_mm_batched(int64_t nbatch, const int32_t* rows, const 
                                      hipStream_t stream);
 
 /*
+ * Load-time preparation of a fused per-tensor weight ([P3] key source
+ * excerpts: the weights-after-loading step requantizes the fused weight to
+ * its largest partition scale, then broadcasts scalar scales per channel when
+ * the rowwise GEMM consumes them).  The weight's N rows are split into nparts
+ * (1..16) logical partitions of widths[i] consecutive rows (a HOST int64
+ * array summing to N; e.g. the Q, K and V blocks of a fused projection), row
+ * block i quantized with the device fp32 scale scales[i] > 0.
+ *
+ * fp8sm_requantize_max_scale: s_max = max_i scales[i] is written to the
+ * device float *max_scale, and every code is requantized against it:
+ *   q'[n][k] = E4M3(clamp(RN32(RN32(dec(w[n][k]) * s_i) * RN32(1 / s_max)), +-448))
+ * for n in partition i (codes of a partition whose scale is s_max are
+ * unchanged).  w, q: device uint8 [N][ldw] / [N][ldq], K % 16 == 0, ldw and
+ * ldq multiples of 16, 16-byte aligned; q == w (with ldq == ldw) converts in
+ * place, other overlaps are not allowed.  NaN codes are not specified.
+ * Errors: widths NULL -> ERR_NULL; nparts out of 1..16 -> ERR_RANGE; a
+ * negative width or a sum != N -> ERR_SHAPE; alignment -> ERR_ALIGN.
+ */
+fp8sm_status fp8sm_requantize_max_scale(const uint8_t* w, int64_t ldw, int64_t N, int64_t K,
+                                        const int64_t* widths, int32_t nparts,
+                                        const float* scales, uint8_t* q, int64_t ldq,
+                                        float* max_scale, hipStream_t stream);
+
+/*
+ * Per-partition scalars broadcast per output channel: out[n] = scales[i] for
+ * every row n of partition i (widths: HOST int64 [nparts], nparts 1..16).
+ * scales: device fp32 [nparts]; out: device fp32 [sum of widths].  To give
+ * every channel the requantized scale, pass max_scale with nparts = 1 and the
+ * total width.
+ */
+fp8sm_status fp8sm_scales_to_channelwise(const float* scales, const int64_t* widths,
+                                         int32_t nparts, float* out, hipStream_t stream);
+
+/*
  * The fused product alone, in fp32: y[m][k] = RN32(silu(x[m][k]) * x[m][K_out+k])
  * with the same silu as fp8sm_quant_group's FUSE_SILU_MUL ([P4] Modifications
  * 2).  x: device bf16/fp16 [M][ld_x], ld_x >= 2*K_out; y: device fp32

@@ -178,6 +178,38 @@ def test_batched_calls_reject_bad_batches_before_any_launch():
     assert mb(A=0) == E["ERR_NULL"]
 
 
+def test_weight_preparation_rejects_bad_arguments():
+    from column_scaled_gemm_amd import fp8sm
+    lib = fp8sm.lib()
+    E = {v: k for k, v in fp8sm.STATUS.items()}
+    P = ctypes.c_void_p
+
+    def rq(widths=(4, 4), N=8, K=32, ldw=32, ldq=32, w=16, q=32, s=16, m=16):
+        arr = (ctypes.c_int64 * max(1, len(widths)))(*widths)
+        return lib.fp8sm_requantize_max_scale(P(w), ldw, N, K, arr, len(widths), P(s), P(q), ldq,
+                                              P(m), P(0))
+    assert rq(widths=()) == E["ERR_RANGE"]
+    assert rq(widths=(1,) * 17, N=17) == E["ERR_RANGE"]
+    assert rq(widths=(4, 3)) == E["ERR_SHAPE"]                # sum != N
+    assert rq(widths=(9, -1)) == E["ERR_SHAPE"]
+    assert rq(K=24, ldw=32, ldq=32) == E["ERR_ALIGN"]          # K % 16
+    assert rq(ldq=16) == E["ERR_SHAPE"]                       # ld < K
+    assert rq(q=16, ldq=48) == E["ERR_SHAPE"]                 # in place needs ldq == ldw
+    assert rq(s=0) == E["ERR_NULL"] and rq(w=0) == E["ERR_NULL"]
+    assert rq(w=8) == E["ERR_ALIGN"]
+    assert lib.fp8sm_requantize_max_scale(P(16), 32, 8, 32, None, 2, P(16), P(32), 32, P(16),
+                                          P(0)) == E["ERR_NULL"]
+
+    def cw(widths=(2, 3), s=16, o=16):
+        arr = (ctypes.c_int64 * max(1, len(widths)))(*widths)
+        return lib.fp8sm_scales_to_channelwise(P(s), arr, len(widths), P(o), P(0))
+    assert cw(widths=()) == E["ERR_RANGE"]
+    assert cw(widths=(2, -3)) == E["ERR_SHAPE"]
+    assert cw(widths=(0, 0)) == E["OK"]
+    assert cw(o=0) == E["ERR_NULL"]
+    assert cw(o=2) == E["ERR_ALIGN"]
+
+
 def test_variant_table_routes_decode_shapes_by_m():
     from column_scaled_gemm_amd import fp8sm
     assert fp8sm.variant_count() >= 3
