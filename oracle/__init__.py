@@ -31,6 +31,9 @@ title and section):
                partition scale, and the per-partition scalar broadcast to
                per-channel scales (prhub digest of PR #33148, key source
                excerpts).
+* ``scatter`` -- the 1x128 group quant with a scattered output: each token's
+               codes and scales written to its top-k destination rows
+               (PR #33533 commit messages, the scatter fusion).
 * ``batched`` -- the batched / masked forms: each batch's live rows (a
                per-batch count, clamped to the slab) go through the 2-D
                definitions with that batch's operands (PR #33533 commit
