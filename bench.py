@@ -158,6 +158,7 @@ def suite(reps):
     """One JSON line per hot-path row.  Quant and decode rows are cold (each
     launch reads its inputs from HBM); the rowwise and blockwise GEMMs, which
     are compute-bound, are warm."""
+    import numpy as np
     import torch
     from column_scaled_gemm_amd import fp8sm, inputs
     dev = torch.device("cuda:0")
@@ -306,6 +307,30 @@ def suite(reps):
          hbm_frac=round(ebytes / us_e / 1e3 / PEAK_HBM, 3),
          TFLOPs=round(2.0 * live * H * I / us_e / 1e6, 1), cache="cold", host_bound=hb)
     del wqs, wss, q, es, c
+    torch.cuda.empty_cache()
+
+    # f3: 1x128 UE8M0 quant scattered to the top-k destination rows of the
+    # grouped-GEMM input (MN-major scales); stand-in: 1024 tokens of hidden
+    # 7168, top-8, 8192 destination rows (the pages print no shapes)
+    Ts, Ks, topk = 1024, inputs.FUSED_K, 8
+    Rs = Ts * topk
+    nrot = _rotations(2 * Ts * Ks + Rs * Ks, True)
+    gen = inputs.rng(50)
+    xs_ = [inputs.to_dtype(gen.standard_normal((Ts, Ks), dtype=np.float32)).to(dev)
+           for _ in range(nrot)]
+    dsts = [torch.from_numpy(gen.permutation(Rs).reshape(Ts, topk).astype(np.int32)).to(dev)
+            for _ in range(nrot)]
+    qs_ = [torch.empty((Rs, Ks), dtype=torch.uint8, device=dev) for _ in range(nrot)]
+    ss_ = torch.empty((Ks // 128, Rs), dtype=torch.uint8, device=dev)
+    us_sc, hb = _time_launches(
+        lambda i: fp8sm.quant_group_scatter(xs_[i % nrot], dsts[i % nrot], Rs, q=qs_[i % nrot],
+                                            scales=ss_, stream=stream),
+        max(reps, nrot), nrot, stream)
+    scb = 2 * Ts * Ks + Rs * Ks + Rs * (Ks // 128) + 4 * Rs
+    emit("f3 scatter 1x128 UE8M0 quant", workload=f"bf16[{Ts},{Ks}] top-{topk} -> {Rs} rows",
+         us=round(us_sc, 2), GBps=round(scb / us_sc / 1e3, 1),
+         hbm_frac=round(scb / us_sc / 1e3 / PEAK_HBM, 3), cache="cold", host_bound=hb)
+    del xs_, dsts, qs_, ss_
     torch.cuda.empty_cache()
 
     # f4: load-time requantization of the fused QKV weight to its largest

@@ -162,6 +162,44 @@ fp8sm_status fp8sm_quant_group_batched(const void* x, fp8sm_dtype in, int64_t nb
                           bs_q, ld_q, scales, stream);
 }
 
+fp8sm_status fp8sm_quant_group_scatter(const void* x, fp8sm_dtype in, int64_t T, int64_t K,
+                                       int64_t ld_x, const int32_t* dst, int32_t topk, int64_t R,
+                                       fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, uint8_t* q,
+                                       int64_t ld_q, void* scales, hipStream_t stream) {
+  if (in != FP8SM_BF16 && in != FP8SM_FP16) return FP8SM_ERR_UNSUPPORTED;
+  if (fmt != FP8SM_SCALE_FP32 && fmt != FP8SM_SCALE_UE8M0_FP32 && fmt != FP8SM_SCALE_UE8M0_BYTE)
+    return FP8SM_ERR_UNSUPPORTED;
+  if (lay != FP8SM_LAYOUT_ROW_MAJOR && lay != FP8SM_LAYOUT_MN_MAJOR) return FP8SM_ERR_UNSUPPORTED;
+  if (T < 0 || R < 0 || K <= 0 || topk < 0) return FP8SM_ERR_SHAPE;
+  if (T > kMaxDim || R > kMaxDim || K > kMaxDim || topk > 1024) return FP8SM_ERR_RANGE;
+  if (K % 128) return FP8SM_ERR_SHAPE;
+  if (ld_x < K || ld_q < K) return FP8SM_ERR_SHAPE;
+  if (ld_x % 8 || ld_q % 8) return FP8SM_ERR_ALIGN;
+  if (T == 0 || topk == 0 || R == 0) return FP8SM_OK;
+  if (!x || !dst || !q || !scales) return FP8SM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(dst, 4) ||
+      !aligned(scales, fmt == FP8SM_SCALE_UE8M0_BYTE ? 1 : 4))
+    return FP8SM_ERR_ALIGN;
+  fp8sm_status st = check_device();
+  if (st != FP8SM_OK) return st;
+  ScatterArgs a;
+  a.x = x;
+  a.f16 = in == FP8SM_FP16;
+  a.T = T;
+  a.K = K;
+  a.ld_x = ld_x;
+  a.dst = dst;
+  a.topk = topk;
+  a.R = R;
+  a.fmt = (int)fmt;
+  a.mn_major = lay == FP8SM_LAYOUT_MN_MAJOR;
+  a.rpad = ((R + 3) / 4) * 4;
+  a.q = q;
+  a.ld_q = ld_q;
+  a.scales = scales;
+  return launched(launch_quant_scatter(a, stream));
+}
+
 static fp8sm_status quant_static_impl(const void* x, fp8sm_dtype in, int64_t nbatch, int64_t M,
                                       int64_t K, int64_t bs_x, int64_t ld_x, const float* scale,
                                       uint8_t* q, int64_t bs_q, int64_t ld_q,

@@ -44,6 +44,22 @@ struct QuantArgs {
 };
 
 hipError_t launch_quant_group(const QuantArgs& a, hipStream_t s);
+
+struct ScatterArgs {
+  const void* x;
+  bool f16;
+  int64_t T, K, ld_x;
+  const int32_t* dst;  // device [T][topk]
+  int topk;
+  int64_t R;           // rows of q
+  int fmt;
+  int mn_major;
+  int64_t rpad;
+  uint8_t* q;
+  int64_t ld_q;
+  void* scales;
+};
+hipError_t launch_quant_scatter(const ScatterArgs& a, hipStream_t s);
 hipError_t launch_quant_static(const void* x, bool f16, int64_t M, int64_t K, int64_t ld_x,
                                const float* scale, uint8_t* q, int64_t ld_q, hipStream_t s,
                                const QuantBatch& bt = QuantBatch{1, 0, 0, 0, nullptr});

@@ -88,24 +88,31 @@ __device__ __forceinline__ void load_values(const uint4 gv, const uint4 uv, floa
   }
 }
 
-// Quantize one 1x128 group held by a 16-lane quarter (8 values per lane) and
-// store its codes and scale.
+// Codes of one 1x128 group held by a 16-lane quarter (8 values per lane), and
+// its scale (value and UE8M0 byte).  Every lane of the quarter takes part.
+template <int FMT>
+__device__ __forceinline__ uint2 group128_codes(float* y, float* sval, int* eb) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
+  amax = group_max<16>(amax);
+  const float mult = group_multiplier<FMT>(amax, sval, eb);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = y[i] * mult;
+  return to_e4m3_x8(y);
+}
+
+// Quantize one 1x128 group and store its codes and scale (row < 0: nothing).
 template <int FMT>
 __device__ __forceinline__ void quant_group128(float* y, int l16, int64_t row, int64_t grp,
                                                uint8_t* __restrict__ q, int64_t ld_q,
                                                void* __restrict__ scales, int64_t G,
                                                int mn_major, int64_t mpad) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
-  amax = group_max<16>(amax);
   float sval;
   int eb;
-  const float mult = group_multiplier<FMT>(amax, &sval, &eb);
+  const uint2 codes = group128_codes<FMT>(y, &sval, &eb);
   if (row >= 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = y[i] * mult;
-    *reinterpret_cast<uint2*>(q + row * ld_q + grp * 128 + l16 * 8) = to_e4m3_x8(y);
+    *reinterpret_cast<uint2*>(q + row * ld_q + grp * 128 + l16 * 8) = codes;
     if (l16 == 0) {
       const int64_t idx = mn_major ? grp * mpad + row : row * G + grp;
       store_scale<FMT>(scales, idx, sval, eb);
@@ -170,6 +177,52 @@ __global__ __launch_bounds__(256) void quant_g128_kernel(
     float y[8];
     widen8<F16>(gv[u], y);
     quant_group128<FMT>(y, l16, row[u], grp[u], q, ld_q, scales, G, mn_major, mpad);
+  }
+}
+
+// 1x128 groups with a scattered output (sglang PR #33533, commit messages: the
+// scatter fusion): token t's groups are quantized once, as above, and each
+// group's codes and scale go to every destination row d = dst[t][j] with
+// 0 <= d < R (the bound is checked here: other entries name no row).  The 16
+// lanes of a quarter read the same destination list (one cache line).
+template <bool F16, int FMT>
+__global__ __launch_bounds__(256) void quant_g128_scatter_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int64_t G, int64_t ld_x,
+    const int32_t* __restrict__ dst, int topk, int64_t R, uint8_t* __restrict__ q, int64_t ld_q,
+    void* __restrict__ scales, int mn_major, int64_t rpad) {
+  const int lane = threadIdx.x & 63;
+  const int quarter = lane >> 4;
+  const int l16 = lane & 15;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t total = T * G;
+  uint4 gv[kQuads];
+  int64_t tok[kQuads], grp[kQuads];
+#pragma unroll
+  for (int u = 0; u < kQuads; ++u) {
+    const int64_t gid = (wave * kQuads + u) * 4 + quarter;
+    tok[u] = -1;
+    grp[u] = 0;
+    gv[u] = make_uint4(0, 0, 0, 0);
+    if (gid < total) {
+      tok[u] = gid / G;
+      grp[u] = gid - tok[u] * G;
+      gv[u] = load_stream16(x + tok[u] * ld_x + grp[u] * 128 + l16 * 8);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kQuads; ++u) {
+    float y[8], sval;
+    int eb;
+    widen8<F16>(gv[u], y);
+    const uint2 codes = group128_codes<FMT>(y, &sval, &eb);
+    if (tok[u] < 0) continue;
+    const int32_t* dl = dst + tok[u] * topk;
+    for (int j = 0; j < topk; ++j) {
+      const int64_t d = dl[j];
+      if (d < 0 || d >= R) continue;
+      *reinterpret_cast<uint2*>(q + d * ld_q + grp[u] * 128 + l16 * 8) = codes;
+      if (l16 == 0) store_scale<FMT>(scales, mn_major ? grp[u] * rpad + d : d * G + grp[u], sval, eb);
+    }
   }
 }
 
@@ -718,6 +771,24 @@ static hipError_t launch_g128(int fmt, const QuantArgs& a, hipStream_t s) {
                        0, s, x, a.M, G, a.ld_x, a.q, a.ld_q, a.scales, a.mn_major, a.mpad,
                        a.batch);
   });
+}
+
+template <bool F16>
+static hipError_t launch_g128_scatter(int fmt, const ScatterArgs& a, hipStream_t s) {
+  const int64_t G = a.K / 128;
+  const int64_t waves = (a.T * G + 15) / 16;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  return with_fmt(fmt, [&](auto f) {
+    constexpr int FMT = decltype(f)::value;
+    hipLaunchKernelGGL((quant_g128_scatter_kernel<F16, FMT>), dim3((unsigned)((waves + 3) / 4)),
+                       dim3(256), 0, s, x, a.T, G, a.ld_x, a.dst, a.topk, a.R, a.q, a.ld_q,
+                       a.scales, a.mn_major, a.rpad);
+  });
+}
+
+hipError_t launch_quant_scatter(const ScatterArgs& a, hipStream_t s) {
+  if (a.T == 0 || a.topk == 0) return hipSuccess;
+  return a.f16 ? launch_g128_scatter<true>(a.fmt, a, s) : launch_g128_scatter<false>(a.fmt, a, s);
 }
 
 template <bool F16>

@@ -36,6 +36,8 @@ SIGNATURES = {
     "fp8sm_scaled_mm_ex": (_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _int, _p, _int, _p,
                                   _p, _int, _p]),
     "fp8sm_silu_mul_f32": (_int, [_p, _int, _i64, _i64, _i64, _p, _i64, _p]),
+    "fp8sm_quant_group_scatter": (_int, [_p, _int, _i64, _i64, _i64, _p, _i32, _i64, _int, _int, _p,
+                                         _i64, _p, _p]),
     "fp8sm_requantize_max_scale": (_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _p, _i64, _p, _p]),
     "fp8sm_scales_to_channelwise": (_int, [_p, _p, _i32, _p, _p]),
     "fp8sm_quant_group_batched": (_int, [_p, _int, _i64, _i64, _i64, _i64, _i64, _p, _i32, _u32,
@@ -376,3 +378,26 @@ def scales_to_channelwise(scales, widths, out=None, stream=None):
     st = _load().fp8sm_scales_to_channelwise(_ptr(scales), arr, n, _ptr(out), _stream(stream))
     _check(st, "fp8sm_scales_to_channelwise")
     return out
+
+
+def quant_group_scatter(x, dst, R, fmt=SCALE_UE8M0_BYTE, layout=LAYOUT_MN_MAJOR, q=None,
+                        scales=None, stream=None):
+    """x [T, K] bf16/fp16 tokens, dst device int32 [T, topk] destination rows
+    -> (codes uint8 [R, K], scales) with each token's 1x128 group quant
+    written to its destination rows (other rows untouched)."""
+    T, K = x.shape
+    _unit_last(x, "x")
+    if dst.dtype != torch.int32 or dst.dim() != 2 or dst.shape[0] != T or not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous int32 [T, topk] tensor")
+    if q is None:
+        q = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        dt = torch.uint8 if fmt == SCALE_UE8M0_BYTE else torch.float32
+        scales = torch.empty(scale_shape(fmt, layout, R, K, 128), dtype=dt, device=x.device)
+    if scales.numel() * scales.element_size() < scale_bytes(fmt, layout, R, K, 128):
+        raise ValueError("scales too small")
+    st = _load().fp8sm_quant_group_scatter(_ptr(x), _dtype_code(x), T, K, x.stride(0), _ptr(dst),
+                                           dst.shape[1], R, fmt, layout, _ptr(q), q.stride(0),
+                                           _ptr(scales), _stream(stream))
+    _check(st, "fp8sm_quant_group_scatter")
+    return q, scales

@@ -109,6 +109,26 @@ fp8sm_status fp8sm_quant_group(const void* x, fp8sm_dtype in, int64_t M, int64_t
                                uint8_t* q, int64_t ld_q, void* scales, hipStream_t stream);
 
 /*
+ * 1x128 group quant with a scattered output ([P4] commit messages: the
+ * scatter fusion of the EP-MoE path).  Token t (row t of x, T rows of K
+ * values, K % 128 == 0) is quantized exactly as fp8sm_quant_group quantizes a
+ * row with group 128, once; its codes and scales are then written to every
+ * destination row d = dst[t][j] (j < topk) with 0 <= d < R of the R-row
+ * output: q row d, and scale row d of a fp8sm_scale_bytes(fmt, lay, R, K, 128)
+ * buffer (MN-major: [G][R_pad], the grouped GEMM's layout).  Entries of dst
+ * outside [0, R) name no row and are skipped (checked on the device); rows no
+ * entry names are not written.  Destinations must be distinct (a row named
+ * twice is written by two threads: not defined).
+ *   dst  device int32 [T][topk], 4-byte aligned; topk 0..1024.
+ *   x, q, ld_x, ld_q, in, fmt, lay as fp8sm_quant_group (ld_x >= K).
+ * Errors as fp8sm_quant_group; K % 128 != 0 -> ERR_SHAPE.
+ */
+fp8sm_status fp8sm_quant_group_scatter(const void* x, fp8sm_dtype in, int64_t T, int64_t K,
+                                       int64_t ld_x, const int32_t* dst, int32_t topk, int64_t R,
+                                       fp8sm_scale_fmt fmt, fp8sm_scale_layout lay, uint8_t* q,
+                                       int64_t ld_q, void* scales, hipStream_t stream);
+
+/*
  * Static per-tensor quant with a checkpoint scale ([P3] motivation and key
  * source excerpts: one scalar activation scale per layer):
  *   q = E4M3(clamp(RN32(x * RN32(1/s)), +-448)).

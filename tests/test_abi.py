@@ -210,6 +210,24 @@ def test_weight_preparation_rejects_bad_arguments():
     assert cw(o=2) == E["ERR_ALIGN"]
 
 
+def test_scatter_quant_rejects_bad_arguments():
+    from column_scaled_gemm_amd import fp8sm
+    lib = fp8sm.lib()
+    E = {v: k for k, v in fp8sm.STATUS.items()}
+    P = ctypes.c_void_p
+
+    def sc(x=16, T=4, K=256, ldx=256, dst=16, topk=2, R=8, fmt=2, lay=1, q=16, ldq=256, s=16):
+        return lib.fp8sm_quant_group_scatter(P(x), 0, T, K, ldx, P(dst), topk, R, fmt, lay, P(q),
+                                             ldq, P(s), P(0))
+    assert sc(K=200, ldx=200, ldq=200) == E["ERR_SHAPE"]      # K % 128
+    assert sc(topk=-1) == E["ERR_SHAPE"] and sc(topk=1025) == E["ERR_RANGE"]
+    assert sc(ldq=128) == E["ERR_SHAPE"]
+    assert sc(fmt=5) == E["ERR_UNSUPPORTED"] and sc(lay=3) == E["ERR_UNSUPPORTED"]
+    assert sc(dst=0) == E["ERR_NULL"]
+    assert sc(dst=2) == E["ERR_ALIGN"]
+    assert sc(T=0) == E["OK"] and sc(topk=0) == E["OK"] and sc(R=0) == E["OK"]
+
+
 def test_variant_table_routes_decode_shapes_by_m():
     from column_scaled_gemm_amd import fp8sm
     assert fp8sm.variant_count() >= 3
