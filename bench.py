@@ -17,6 +17,7 @@ same workload (a block of rows: their per-token quant plus their GEMM rows).
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -102,11 +103,16 @@ def cpu_baseline(w, M, N, K, target_s):
         t = run(R)
         if t >= 0.5 * target_s or R == M:
             break
+    passes = 1
+    if R == M and t < 0.5 * target_s:  # the whole workload is short: repeat it
+        passes = int(math.ceil(target_s / max(t, 1e-3)))
+        t = sum(run(R) for _ in range(passes))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(2.0 * R * N * K / t / 1e12, 6), "unit": "TFLOP/s",
+    what = f"first {R} of {M} rows" if R < M else f"all {M} rows x {passes} passes"
+    return {"value": round(2.0 * passes * R * N * K / t / 1e12, 6), "unit": "TFLOP/s",
             "cores": int(threads), "kind": "oracle",
-            "sample": f"first {R} of {M} rows: per-token quant + GEMM rows vs the full "
-                      f"{N}x{K} weight ({t:.1f} s)"}
+            "sample": f"{what}: per-token quant + GEMM rows vs the full {N}x{K} weight "
+                      f"({t:.1f} s)"}
 
 
 def _time_launches(fn, reps, nrot, stream, batches=3):
