@@ -221,6 +221,10 @@ __device__ __forceinline__ void tile_coords(int bid, int nbid, int tiles_m, int 
   tn = r / gm;
 }
 
+// Fourth word of a raw buffer resource on gfx9-family chips (gfx950): 32-bit
+// data format, no swizzle, no per-lane index.
+constexpr int kBufferWord3 = 0x00020000;
+
 // 16 zero bytes: the DMA source for chunk positions past K.
 __device__ __attribute__((aligned(16))) uint8_t g_zero16[16];
 
@@ -582,11 +586,21 @@ __global__ __launch_bounds__(64) void gemm_decode_kernel(
   uint32_t ao[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) ao[i] = (uint32_t)(min(16 * i + r16, M - 1) * lda + kl);
+  // Buffer loads: the wave-uniform panel base and the chunk offset stay in
+  // scalar registers, so a load costs no vector address arithmetic (offsets
+  // are below 2^31: K <= 65536 and 64 rows of at most 64 KiB; the record
+  // count never clamps).
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)bbase, (short)0, 0x7FFFFFFF, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0x7FFFFFFF, kBufferWord3);
   auto ldb16 = [&](int kc) -> uint4 {
-    return *reinterpret_cast<const uint4*>(bbase + (int64_t)kc * kChunk + bo);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsb, (int)bo, kc * kChunk, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
   };
   auto lda16 = [&](int i, int kc) -> uint4 {
-    return *reinterpret_cast<const uint4*>(A + (int64_t)kc * kChunk + ao[i]);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsa, (int)ao[i], kc * kChunk, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
   };
   f32x4 acc[TM][1];
 #pragma unroll

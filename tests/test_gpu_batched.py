@@ -361,3 +361,59 @@ def test_masked_moe_pipeline_graph_replays():
         for e in range(E):
             assert np.array_equal(qh[e, :cnt[e]], ref[e].codes), e
             assert_within_tolerance(cg[e, :cnt[e]], res[e], inter, f"replay {cnt} e={e}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_linear_graph_replays_strided_bias_k80(out_dtype):
+    # the deterministic static-FP8 linear of sglang PR #44861 (Modifications:
+    # graph replays with bias, strided 3-D inputs, BF16/FP16 and a K = 80 tail):
+    # static quant of a strided [B, S, K] activation, then the batched GEMM
+    # against one per-tensor weight with a bias, captured once and replayed
+    # with new activations; every replay equals the eager call bitwise and the
+    # oracle within the bound
+    B, S, K, N = 3, 7, 80, 96
+    r = inputs.rng(80)
+    w = inputs.to_dtype(r.standard_normal((N, K), dtype=np.float32) * F32(0.02))
+    ws = F32(inputs.static_scale(w))
+    wq = ob.quant_static_batched(inputs.widen(w)[None], ws)[0]
+    bias = inputs.to_dtype(r.standard_normal(N, dtype=np.float32), out_dtype)
+    xs = [inputs.to_dtype(r.standard_normal((B, S, K), dtype=np.float32)) for _ in range(3)]
+    xsc = F32(max(inputs.static_scale(x) for x in xs))
+    xv = _strided_3d(xs[0], B, S)
+    wd, sx, sw = torch.from_numpy(wq).to(cuda()), torch.tensor([xsc], device=cuda()), torch.tensor([ws], device=cuda())
+    bd = bias.to(cuda())
+    q = torch.empty((B, S, K), dtype=torch.uint8, device=cuda())
+    c = torch.empty((B, S, N), dtype=out_dtype, device=cuda())
+
+    def step(stream=None):
+        fp8sm.quant_static_batched(xv, sx, q=q, stream=stream)
+        fp8sm.scaled_mm_batched(q, wd, sx, sw, T, T, c=c, bias=bd, out_dtype=out_dtype, stream=stream)
+
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        step(cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    out = "fp16" if out_dtype == torch.float16 else "bf16"
+    for x in xs + xs[:1]:
+        xv.copy_(x.to(cuda()))
+        c.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        cg = bf16_bits(c)
+        c.zero_()
+        step()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(c), cg)
+        qa = ob.quant_static_batched(inputs.widen(x), xsc)
+        assert np.array_equal(q.cpu().numpy(), qa)
+        res = ob.scaled_mm_batched(qa, wq, np.full(B, xsc, F32), np.full(B, ws, F32),
+                                   bias=bias.float().numpy(), out=out)
+        for b in range(B):
+            assert_within_tolerance(cg[b], res[b], K, f"graph replay {out} b={b}")
