@@ -144,11 +144,13 @@ def quant_group(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul
                 q=None, scales=None, stream=None):
     """x [M, K_in] bf16/fp16 (K_in = 2*K_out when fused) -> (codes uint8 [M, K_out], scales)."""
     M, K_in = x.shape
+    _unit_last(x, "x")
     K_out = K_in // 2 if fuse_silu_mul else K_in
     if group == -1:
         group = K_out
     if q is None:
         q = torch.empty((M, K_out), dtype=torch.uint8, device=x.device)
+    _unit_last(q, "q")
     if scales is None:
         dt = torch.uint8 if fmt == SCALE_UE8M0_BYTE else torch.float32
         scales = torch.empty(scale_shape(fmt, layout, M, K_out, group), dtype=dt, device=x.device)
@@ -162,8 +164,10 @@ def quant_group(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul
 def quant_static(x, scale, q=None, stream=None):
     """x [M, K] bf16/fp16, scale: 1-element fp32 device tensor -> codes [M, K]."""
     M, K = x.shape
+    _unit_last(x, "x")
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    _unit_last(q, "q")
     st = _load().fp8sm_quant_static(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(scale),
                                     _ptr(q), q.stride(0), _stream(stream))
     _check(st, "fp8sm_quant_static")
@@ -172,8 +176,10 @@ def quant_static(x, scale, q=None, stream=None):
 
 def quant_weight_block128(w, q=None, scales=None, stream=None):
     N, K = w.shape
+    _unit_last(w, "w")
     if q is None:
         q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    _unit_last(q, "q")
     if scales is None:
         scales = torch.empty(((N + 127) // 128, (K + 127) // 128), dtype=torch.float32,
                              device=w.device)
@@ -186,9 +192,11 @@ def quant_weight_block128(w, q=None, scales=None, stream=None):
 def silu_mul_f32(x, y=None, stream=None):
     """x [M, 2K] bf16/fp16 [gate | up] -> y [M, K] fp32 = silu(gate) * up."""
     M, K2 = x.shape
+    _unit_last(x, "x")
     K = K2 // 2
     if y is None:
         y = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    _unit_last(y, "y")
     st = _load().fp8sm_silu_mul_f32(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(y),
                                     y.stride(0), _stream(stream))
     _check(st, "fp8sm_silu_mul_f32")
@@ -203,10 +211,13 @@ def scaled_mm(a, b, sa, sb, kind_a, kind_b, c=None, M=None, stream=None, bias=No
     Mx, K = a.shape
     M = Mx if M is None else M
     N = b.shape[0]
+    _unit_last(a, "a")
+    _unit_last(b, "b")
     if out_dtype is None:
         out_dtype = c.dtype if c is not None else torch.bfloat16
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=b.device)
+    _unit_last(c, "c")
     if bias is None and out_dtype == torch.bfloat16:
         st = _load().fp8sm_scaled_mm(_ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(c),
                                      c.stride(0), M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb),

@@ -244,3 +244,19 @@ def test_variant_table_routes_decode_shapes_by_m():
     finally:
         fp8sm.force_variant(prev)
     assert fp8sm.pick_variant(8320, 21504, 5376) == fp8sm.pick_variant(8320, 21504, 5376)
+
+
+def test_binding_rejects_views_with_a_strided_last_dimension():
+    # the C ABI takes one row stride; a view whose elements are not contiguous
+    # within a row must not reach it (checked before any call)
+    import torch
+    from column_scaled_gemm_amd import fp8sm
+    x = torch.zeros(4, 512, dtype=torch.bfloat16)[:, ::2]
+    codes = torch.zeros(8, 64, dtype=torch.uint8)
+    for call in (lambda: fp8sm.quant_group(x, 128),
+                 lambda: fp8sm.quant_static(x, torch.ones(1)),
+                 lambda: fp8sm.scaled_mm(codes[:, ::2], codes[:, :32], torch.ones(1), torch.ones(1),
+                                         fp8sm.KIND_TENSOR, fp8sm.KIND_TENSOR),
+                 lambda: fp8sm.quant_group_batched(x[None], 128)):
+        with pytest.raises(ValueError):
+            call()
