@@ -417,3 +417,23 @@ def test_linear_graph_replays_strided_bias_k80(out_dtype):
                                    bias=bias.float().numpy(), out=out)
         for b in range(B):
             assert_within_tolerance(cg[b], res[b], K, f"graph replay {out} b={b}")
+
+
+def test_largest_batch_count_sampled():
+    # 65535 batches (one grid row each), per-batch weights and scalar scales;
+    # sampled batches against the oracle and the 2-D call
+    B, M, N, K = 65535, 2, 16, 32
+    A = inputs.random_codes((B, M, K), seed=11) & 0x77
+    W = inputs.random_codes((B, N, K), seed=12) & 0x77
+    r = inputs.rng(13)
+    sa = np.exp2(r.integers(-4, 4, B)).astype(F32)
+    sb = np.exp2(r.integers(-4, 4, B)).astype(F32)
+    c = fp8sm.scaled_mm_batched(torch.from_numpy(A).to(cuda()), torch.from_numpy(W).to(cuda()),
+                                torch.from_numpy(sa).to(cuda()), torch.from_numpy(sb).to(cuda()),
+                                T, T)
+    torch.cuda.synchronize()
+    got = bf16_bits(c)
+    pick = [0, 1, 255, 256, 32767, 65533, 65534]
+    res = ob.scaled_mm_batched(A[pick], W[pick], sa[pick], sb[pick])
+    for i, b in enumerate(pick):
+        assert_within_tolerance(got[b], res[i], K, f"batch {b} of {B}")

@@ -369,3 +369,37 @@ def test_full_size_rowwise_sampled(name):
 @pytest.mark.parametrize("name", ["mlp_gateup_23216", "mlp_gateup_15760"])
 def test_full_size_rowwise_sampled_large(name):
     _sampled_full_size(name)
+
+
+def test_max_k_rowwise_every_variant():
+    # K = 65536, the largest the boundary takes: every variant within the
+    # bound and bitwise equal
+    M, N, K = 37, 72, 65536
+    print(f"[case] max K M={M} N={N} K={K}", flush=True)
+    A, B, sa, sb = _quantized_case(M, N, K, seed=5)
+    res = og.scaled_mm(A, B, sa, sb)
+    outs = {}
+    for v in _variants_for(M):
+        outs[v] = _mm_variant(v, A, B, sa, sb)
+        assert_within_tolerance(outs[v], res, K, f"max K {fp8sm.variant_name(v)}")
+    first = next(iter(outs.values()))
+    assert all(np.array_equal(o, first) for o in outs.values())
+
+
+@pytest.mark.parametrize("shape", [(70, 264, 8320), (20, 128, 65536)])
+def test_blockwise_ue8m0_long_k_restages_scales(shape):
+    # more than 64 K blocks: the kernel re-stages the activation scale bytes
+    # every 64 blocks; the last segment is partial
+    M, N, K = shape
+    print(f"[case] blockwise long K M={M} N={N} K={K}", flush=True)
+    r = inputs.rng(K + M)
+    G = (K + 127) // 128
+    A = inputs.random_codes((M, K), seed=M + 1)
+    B = inputs.random_codes((N, K), seed=N + 1)
+    e = r.integers(119, 131, size=(M, G)).astype(np.uint8)
+    sb = np.exp2(r.uniform(-14, -6, ((N + 127) // 128, G))).astype(F32)
+    c = fp8sm.scaled_mm(to_gpu_u8(A), to_gpu_u8(B), torch.from_numpy(e).to(cuda()),
+                        to_gpu_f32(sb), fp8sm.KIND_GROUP128_UE8M0, fp8sm.KIND_BLOCK128)
+    torch.cuda.synchronize()
+    a_vals = np.exp2(e.astype(np.float64) - 127).astype(F32)
+    assert_within_tolerance(bf16_bits(c), og.blockwise_mm(A, a_vals, B, sb), K, f"long K {shape}")

@@ -188,3 +188,17 @@ def test_fused_workload_full_size(dtype):
 def test_qkv_activation_quant_full_size():
     w = inputs.workload("qkv")
     _check(w.x, -1, fp8sm.SCALE_FP32, fp8sm.LAYOUT_ROW_MAJOR, what="qkv per-token")
+
+
+def test_per_token_quant_max_width():
+    # the longest rows (K = 65536, two-pass kernel), fp32 and UE8M0 scales
+    M, K = 3, 65536
+    r = inputs.rng(65536)
+    x = inputs.to_dtype(r.standard_normal((M, K), dtype=np.float32))
+    for fmt, pow2 in ((fp8sm.SCALE_FP32, False), (fp8sm.SCALE_UE8M0_BYTE, True)):
+        q, s = fp8sm.quant_group(x.to(cuda()), -1, fmt)
+        torch.cuda.synchronize()
+        ref = oq.quant_group(inputs.widen(x), K, pow2=pow2)
+        assert np.array_equal(q.cpu().numpy(), ref.codes)
+        want = ref.ue8m0_byte if pow2 else ref.scale
+        assert np.array_equal(s.cpu().numpy().reshape(-1), want.reshape(-1))
