@@ -226,10 +226,14 @@ __global__ __launch_bounds__(256) void quant_g128_scatter_kernel(
   }
 }
 
-// Fused SiLU-and-mul + 1x128 groups: one 1024-thread workgroup per CU builds
-// the silu table in LDS, then its 16 wavefronts walk the flattened
+// Fused SiLU-and-mul + 1x128 groups: one 1024-thread workgroup per CU copies
+// the silu table into LDS, then its 16 wavefronts walk the flattened
 // (row, group) space 16 groups (kQuads x 4 quarters) per step, loading the
-// next step while converting the current one.  A fused row is [gate | up],
+// next step while converting the current one.  Quads are interleaved across
+// the grid: quad u of wavefront w at step t covers groups
+// ((4 t + u) nw + w) 4 .. + 3 (nw wavefronts in the grid), so consecutive
+// wavefronts take consecutive 4-group runs and a short batch (a masked
+// expert's few rows) spreads over every workgroup instead of a few.  A fused row is [gate | up],
 // each K wide.  M and G are at most 2^30 (checked at the boundary), so rows
 // and groups fit in int.  Each lane keeps a (row, group) cursor per quad and
 // advances it without division; loads past the last row read the last row
@@ -247,29 +251,31 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
     int64_t mpad, QuantBatch bt) {
   __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
   M = (int)enter_batch<FMT>(bt, x, q, scales, M);
-  // a workgroup whose first group is past the batch's groups has no work at
-  // any step: it leaves before copying the table (uniform, before the barrier)
-  if ((int64_t)blockIdx.x * 256 >= (int64_t)M * G) return;
+  // a workgroup whose first group (that of its first wavefront's quad 0 at
+  // step 0) is past the batch's groups has no work at any step: it leaves
+  // before copying the table (uniform, before the barrier)
+  if ((int64_t)blockIdx.x * 64 >= (int64_t)M * G) return;
   const int lane = threadIdx.x & 63;
   const int quarter = lane >> 4;
   const int l16 = lane & 15;
   const int64_t total = (int64_t)M * G;
-  // step w covers flattened groups 16 w .. 16 w + 15; a wavefront's steps are
-  // nw apart, i.e. each cursor moves by 16 nw groups = (drow, dgrp)
+  // g0: first group of this wavefront's quad 0 at the current step; every
+  // step moves each cursor by 16 nw groups = (drow, dgrp)
   const int64_t nw = (int64_t)gridDim.x * 16;
-  int64_t w = (int64_t)blockIdx.x * 16 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t w = (int64_t)blockIdx.x * 16 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t g0 = w * 4;
   int drow, dgrp;
   int cr[kQuads], cc[kQuads];
   if constexpr (O32) {
     // M * G < 2^23 here (the host checked every byte offset against 2^32),
-    // and w * 16 < 256 * gridDim.x: 32-bit divisions are exact and far
-    // cheaper than 64-bit ones
+    // and the first groups are below 16 nw: 32-bit divisions are exact and
+    // far cheaper than 64-bit ones
     const uint32_t ug = (uint32_t)G, step = (uint32_t)nw * 16u;
     drow = (int)(step / ug);
     dgrp = (int)(step - (uint32_t)drow * ug);
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
-      const uint32_t gid = (uint32_t)w * 16u + 4u * u + (uint32_t)quarter;
+      const uint32_t gid = ((uint32_t)u * (uint32_t)nw + (uint32_t)w) * 4u + (uint32_t)quarter;
       cr[u] = (int)(gid / ug);
       cc[u] = (int)(gid - (uint32_t)cr[u] * ug);
     }
@@ -278,7 +284,7 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
     dgrp = (int)(nw * 16 - (int64_t)drow * G);
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
-      const int64_t gid = w * 16 + 4 * u + quarter;
+      const int64_t gid = (u * nw + w) * 4 + quarter;
       cr[u] = (int)(gid / G);
       cc[u] = (int)(gid - (int64_t)cr[u] * G);
     }
@@ -325,12 +331,13 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
   fetch(a);  // the first loads overlap the table build
   SiluTable<F16>::build(tab, threadIdx.x, 1024);
   __syncthreads();
-  while (w * 16 < total) {
-    w += nw;
+  const int64_t step = 16 * nw;
+  while (g0 < total) {
+    g0 += step;
     fetch(b);
     convert(a);
-    if (w * 16 >= total) break;
-    w += nw;
+    if (g0 >= total) break;
+    g0 += step;
     fetch(a);
     convert(b);
   }
