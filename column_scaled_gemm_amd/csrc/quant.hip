@@ -328,8 +328,8 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
     }
   };
   G128Step a, b;
-  fetch(a);  // the first loads overlap the table build
-  SiluTable<F16>::build(tab, threadIdx.x, 1024);
+  fetch(a);  // the first loads overlap the table copy
+  SiluTable<F16>::load(tab, threadIdx.x, 1024);
   __syncthreads();
   const int64_t step = 16 * nw;
   while (g0 < total) {
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(1024) void quant_token_fused_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
   M = enter_batch<FMT>(bt, x, q, scales, M);
   if ((int64_t)blockIdx.x * 16 >= M) return;  // no row for any wavefront (uniform)
-  SiluTable<F16>::build(tab, threadIdx.x, 1024);
+  SiluTable<F16>::load(tab, threadIdx.x, 1024);
   __syncthreads();
   for (int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6); row < M;
        row += (int64_t)gridDim.x * 16)
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(1024) void silu_mul_kernel(const uint16_t* __restri
                                                         int64_t K, int64_t ld_x,
                                                         float* __restrict__ y, int64_t ld_y) {
   __shared__ __attribute__((aligned(16))) uint8_t tab[SiluTable<F16>::kBytes];
-  SiluTable<F16>::build(tab, threadIdx.x, 1024);
+  SiluTable<F16>::load(tab, threadIdx.x, 1024);
   __syncthreads();
   const int64_t nch = K >> 3;
   const int64_t total = M * nch;

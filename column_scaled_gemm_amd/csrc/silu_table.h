@@ -57,7 +57,7 @@ struct SiluTable<false> {
 
   static_assert(sizeof(kSiluBf16Table) == kBytes, "generated bf16 table size");
 
-  __device__ static void build(void* lds, int tid, int nthr) {
+  __device__ static void load(void* lds, int tid, int nthr) {
     copy_table<kBytes>(lds, kSiluBf16Table, tid, nthr);
   }
 
@@ -87,7 +87,7 @@ struct SiluTable<true> {
 
   static_assert(sizeof(kSiluF16Table) == kBytes, "generated fp16 table size");
 
-  __device__ static void build(void* lds, int tid, int nthr) {
+  __device__ static void load(void* lds, int tid, int nthr) {
     copy_table<kBytes>(lds, kSiluF16Table, tid, nthr);
   }
 
