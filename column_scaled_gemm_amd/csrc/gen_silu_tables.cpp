@@ -7,8 +7,8 @@
 //    b = RN32(g / RN32(1 + RN32(e^-g))); E = 100 stands for |g| < 2^-26
 //    (a = 1/2), E = 134 for |g| >= 2^7 (a = 1 for g > 0, 0 for g < 0); b = -0
 //    outside the window.
-//  * fp16: e^-gh and e^+-gl in fp64 per sign, E = 101..134 and 5 mantissa
-//    bits; row 134 holds 0 or +inf and 1.
+//  * fp16: RN32(g / RN32(1 + RN32(e^-g))) for every fp16 pattern with
+//    exponent field 5..21 (2^-10 <= |g| < 2^7), per sign.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -50,27 +50,18 @@ int main() {
   }
   std::printf("};\n");
 
-  const uint32_t e0h = 101, rowsh = 34, half = 2 * rowsh * 32;
-  std::printf("alignas(16) __device__ const double kSiluF16Table[%u] = {\n", 2 * half);
-  double h[2 * 34 * 32], l[2 * 34 * 32];
-  for (uint32_t j = 0; j < half; ++j) {
-    const uint32_t s = j / (rowsh * 32), r = (j / 32) % rowsh, m = j % 32;
-    if (r == rowsh - 1) {
-      h[j] = s ? HUGE_VAL : 0.0;
-      l[j] = 1.0;
-    } else {
-      h[j] = std::exp(-(double)as_float(s << 31 | (r + e0h) << 23 | m << 18));
-      const double gl = std::ldexp((double)m, (int)(r + e0h) - 137);  // m * 2^(E-127-10)
-      l[j] = std::exp(s ? gl : -gl);
-    }
-  }
-  for (uint32_t j = 0; j < half; ++j) {
-    put(h[j]);
-    if (j % 4 == 3) std::printf("\n");
-  }
-  for (uint32_t j = 0; j < half; ++j) {
-    put(l[j]);
-    if (j % 4 == 3) std::printf("\n");
+  // fp16: every pattern with exponent field 5..21, per sign, the same formula
+  const uint32_t lo = 5u << 10, span = 17u << 10;
+  std::printf("alignas(16) __device__ const float kSiluF16Table[%u] = {\n", 2 * span);
+  for (uint32_t j = 0; j < 2 * span; ++j) {
+    const uint32_t s = j / span, mag = lo + j % span;
+    const uint32_t ex = mag >> 10, man = mag & 1023u;  // normal: 1.man x 2^(ex - 15)
+    float g = std::ldexp((float)(1024u + man), (int)ex - 25);
+    if (s) g = -g;
+    const float e = (float)std::exp(-(double)g);
+    const float d = 1.0f + e;
+    put(g / d);
+    if (j % 8 == 7) std::printf("\n");
   }
   std::printf("};\n");
   return 0;

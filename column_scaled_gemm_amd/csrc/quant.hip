@@ -74,8 +74,13 @@ __device__ __forceinline__ void load_values(const uint4 gv, const uint4 uv, floa
     float u[8];
     widen8<F16>(uv, u);
     if constexpr (F16) {
+      // fp16 gates: index the table from the raw 16-bit halves
+      const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = SiluTable<true>::lookup(tab, y[i]) * u[i];
+      for (int i = 0; i < 4; ++i) {
+        y[2 * i] = SiluTable<true>::lookup_bits(tab, y[2 * i], w[i] & 0xFFFFu) * u[2 * i];
+        y[2 * i + 1] = SiluTable<true>::lookup_bits(tab, y[2 * i + 1], w[i] >> 16) * u[2 * i + 1];
+      }
     } else {
       // bf16 gates: index the table from the raw 16-bit halves
       const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
@@ -804,10 +809,8 @@ static hipError_t launch_g128_fused(int fmt, const QuantArgs& a, hipStream_t s) 
   const unsigned blocks = persistent_blocks(16 * 16, a.M * G, a.batch.count);  // 16 waves x 16 groups
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   // every byte offset the kernel forms below 2^32: 32-bit address arithmetic
-  // (bf16 only: the fp16 form, whose lookup holds fp64 temporaries, spills at
-  // its 128-register budget with it and runs faster without)
   const uint64_t lim = (uint64_t)1 << 32;
-  const bool o32 = !F16 && (uint64_t)a.M * (uint64_t)a.ld_x * 2 + 2 * (uint64_t)a.K < lim &&
+  const bool o32 = (uint64_t)a.M * (uint64_t)a.ld_x * 2 + 2 * (uint64_t)a.K < lim &&
                    (uint64_t)a.M * (uint64_t)a.ld_q < lim &&
                    (uint64_t)(a.mn_major ? G * a.mpad : a.M * G) < lim;
   return with_fmt(fmt, [&](auto f) {

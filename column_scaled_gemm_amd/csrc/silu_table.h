@@ -18,16 +18,11 @@
 // silu_f32(g); row E = 100 stands for every |g| < 2^-26 with (1/2, -0); row
 // E = 134 for every |g| >= 2^7 with (1, -0) for g > 0 and (0, -0) for g < 0.
 // A -0 addend keeps the sign of a zero product.  2 x 35 x 128 x 8 = 71680 B.
-// fp16 (11 significant bits, too many for a direct table): e^-g is the
-// product of two fp64 factors, e^-gh * e^-gl, where gh keeps the top five
-// stored mantissa bits of g and gl the next five.  Each factor table has
-// 2 signs x 34 rows (E = 101..134) x 32 entries; row 134 holds e^-gh = 0
-// (g > 0) or +inf (g < 0) and e^-gl = 1, so the upper end of the window needs
-// no branch, and the only fp16 gates below it are +-0.  The
-// product rounded to fp32 is RN32(e^-g).  g / d is formed in fp64 -- the
-// hardware reciprocal, one Newton step, one remainder correction -- and
-// rounded once to fp32: no fp16 gate has g / d closer than 2^-48 (relative)
-// to an fp32 rounding boundary, far above the error of that quotient.  2 x 2 x 34 x 32 x 8 = 34816 B.
+// fp16: a direct table of the fp32 silu for every fp16 gate with
+// 2^-10 <= |g| < 2^7 (exponent field 5..21, 2 x 17408 entries, 139264 B), indexed
+// by the gate's 16-bit pattern.  Outside it: |g| >= 2^7 has the closed forms
+// above; |g| < 2^-10 (zero and the smallest gates) evaluates RN32(e^-g) from
+// the series of e^-g in fp64 and divides in fp32.
 // Both forms are checked against the oracle for every finite gate value of
 // their dtype by the parity tests.  Non-finite gates are not specified.
 #pragma once
@@ -81,9 +76,9 @@ struct SiluTable<false> {
 
 template <>
 struct SiluTable<true> {
-  static constexpr uint32_t kE0 = 101, kRows = 34;  // E = 101 .. 134
-  static constexpr int kHalf = 2 * kRows * 32;      // entries per factor table
-  static constexpr int kBytes = 2 * kHalf * 8;
+  // fp16 patterns with exponent field 5..21 (2^-10 <= |g| < 2^7), per sign
+  static constexpr uint32_t kLo = 5u << 10, kSpan = 17u << 10, kHi = 22u << 10;
+  static constexpr int kBytes = 2 * kSpan * 4;
 
   static_assert(sizeof(kSiluF16Table) == kBytes, "generated fp16 table size");
 
@@ -91,21 +86,30 @@ struct SiluTable<true> {
     copy_table<kBytes>(lds, kSiluF16Table, tid, nthr);
   }
 
+  // Gates outside the table's window.
+  __device__ static float outside(float g, uint32_t mag) {
+    if (mag >= kHi) return g > 0.0f ? g : -0.0f;  // RN32(e^-g) is 0 or +inf
+    // |g| < 2^-10: e^-g by its series in fp64 -- the terms past t^4 are
+    // below 2^-57 of the sum -- then rounded to fp32 once
+    const double t = -(double)g;
+    const double e = 1.0 + t * (1.0 + t * (0.5 + t * (1.0 / 6.0 + t * (1.0 / 24.0))));
+    const float d = 1.0f + (float)e;
+    return g / d;
+  }
+
+  // silu of an fp16 gate g from its 16-bit pattern.  The table read is
+  // branch-free (clamped index); the rare gates outside the window take the
+  // short exact path above.
+  __device__ static float lookup_bits(const void* lds, float g, uint32_t bits) {
+    const uint32_t mag = bits & 0x7FFFu;
+    const uint32_t off = mag - kLo;  // wraps below the window
+    float r = static_cast<const float*>(lds)[(bits >> 15) * kSpan + min(off, kSpan - 1)];
+    if (off >= kSpan) r = outside(g, mag);
+    return r;
+  }
+
   __device__ static float lookup(const void* lds, float g) {
-    const uint32_t b = __float_as_uint(g);
-    const uint32_t e = min(max((b >> 23) & 255u, kE0), kE0 + kRows - 1) - kE0;
-    const uint32_t row = ((b >> 31) * kRows + e) << 5;
-    const double* h = static_cast<const double*>(lds);
-    const double em = h[row | ((b >> 18) & 31u)] * h[kHalf + (row | ((b >> 13) & 31u))];
-    const double d = (double)(1.0f + (float)em);
-    const double g64 = (double)g;
-    double r = __builtin_amdgcn_rcp(d);                 // approximate reciprocal
-    r = __builtin_fma(__builtin_fma(-d, r, 1.0), r, r);  // one Newton step
-    const double q0 = g64 * r;
-    const float q = (float)__builtin_fma(__builtin_fma(-q0, d, g64), r, q0);  // remainder correction
-    // The exact result is a signed zero only for g = +-0 or d = +inf (where the
-    // steps above give +0 or NaN); nowhere else is it zero.
-    return fabsf(q) > 0.0f ? q : g * 0.0f;
+    return lookup_bits(lds, g, (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)g));
   }
 };
 
