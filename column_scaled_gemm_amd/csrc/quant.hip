@@ -76,11 +76,10 @@ __device__ __forceinline__ void load_values(const uint4 gv, const uint4 uv, floa
     if constexpr (F16) {
       // fp16 gates: index the table from the raw 16-bit halves
       const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
+      float sl[8];
+      SiluTable<true>::lookup8(tab, w, y, sl);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        y[2 * i] = SiluTable<true>::lookup_bits(tab, y[2 * i], w[i] & 0xFFFFu) * u[2 * i];
-        y[2 * i + 1] = SiluTable<true>::lookup_bits(tab, y[2 * i + 1], w[i] >> 16) * u[2 * i + 1];
-      }
+      for (int i = 0; i < 8; ++i) y[i] = sl[i] * u[i];
     } else {
       // bf16 gates: index the table from the raw 16-bit halves
       const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};

@@ -56,11 +56,6 @@ struct SiluTable<false> {
     copy_table<kBytes>(lds, kSiluBf16Table, tid, nthr);
   }
 
-  __device__ static float lookup(const void* lds, float g) {
-    const uint32_t b = __float_as_uint(g);
-    return lookup_bits(lds, g, (b >> 16) & 0x7FFFu, b >> 31);
-  }
-
   // The same from the gate's bf16 pattern: mag = its low 15 bits, s = its
   // sign bit.  Clamping mag (positive bf16 patterns order like integers) to
   // [E=100 m=0, E=134 m=127] selects the row and mantissa in one step; the
@@ -97,20 +92,29 @@ struct SiluTable<true> {
     return g / d;
   }
 
-  // silu of an fp16 gate g from its 16-bit pattern.  The table read is
-  // branch-free (clamped index); the rare gates outside the window take the
-  // short exact path above.
-  __device__ static float lookup_bits(const void* lds, float g, uint32_t bits) {
-    const uint32_t mag = bits & 0x7FFFu;
-    const uint32_t off = mag - kLo;  // wraps below the window
-    float r = static_cast<const float*>(lds)[(bits >> 15) * kSpan + min(off, kSpan - 1)];
-    if (off >= kSpan) r = outside(g, mag);
-    return r;
+  // silu of eight fp16 gates (the 16-bit halves of w[0..3], widened in g):
+  // branch-free table reads (clamped index) for all, then one test, so the
+  // common case (every gate inside the window) takes a single branch; the
+  // rare gates outside it take the exact path above.
+  __device__ static void lookup8(const void* lds, const uint32_t (&w)[4], const float* g,
+                                 float* r) {
+    uint32_t mag[8];
+    bool out = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+      mag[i] = bits & 0x7FFFu;
+      const uint32_t off = mag[i] - kLo;
+      out = out || off >= kSpan;
+      r[i] = static_cast<const float*>(lds)[(bits >> 15) * kSpan + min(off, kSpan - 1)];
+    }
+    if (out) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (mag[i] - kLo >= kSpan) r[i] = outside(g[i], mag[i]);
+    }
   }
 
-  __device__ static float lookup(const void* lds, float g) {
-    return lookup_bits(lds, g, (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)g));
-  }
 };
 
 }  // namespace fp8sm
