@@ -47,6 +47,9 @@ inline fp8sm_status launched(hipError_t e) { return e == hipSuccess ? FP8SM_OK :
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxK = 65536;
+// GEMM operand row strides (bytes): the kernels address up to 64 rows of A or
+// B with 32-bit offsets from one base, so 64 * stride + K must stay below 2^31.
+constexpr int64_t kMaxGemmLd = (int64_t)1 << 24;
 constexpr int64_t kMaxBatch = 65535;  // one grid row (blockIdx.y) per batch
 
 // Batch arguments common to every batched call: the count, non-negative
@@ -349,6 +352,7 @@ static fp8sm_status scaled_mm_impl(const uint8_t* A, int64_t lda, const uint8_t*
   if (M < 0 || N < 0 || K < 0) return FP8SM_ERR_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxK) return FP8SM_ERR_RANGE;
   if (lda < K || ldb < K || ldc < N) return FP8SM_ERR_SHAPE;
+  if (lda > kMaxGemmLd || ldb > kMaxGemmLd) return FP8SM_ERR_RANGE;
   if (K % 16 || lda % 16 || ldb % 16 || bt.a % 16 || bt.b % 16) return FP8SM_ERR_ALIGN;
   if (N % 8 || ldc % 8 || bt.c % 8) return FP8SM_ERR_ALIGN;
   if (!disjoint(bt.count, bt.c, M, ldc, N)) return FP8SM_ERR_SHAPE;

@@ -261,6 +261,84 @@ __device__ __forceinline__ int frag32_off(int lane, int q) {
   return (lane & 31) * kChunk + ((((lane >> 5) * 2 + q) ^ swz16(lane & 15)) << 4);
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor starting at base (wave-uniform, so it lives in SGPRs);
+// byte offsets below 2^31 are in range.
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));  // stride field 0
+  r[2] = 0x7FFFFFFF;
+  r[3] = kBufferWord3;
+  return r;
+}
+
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): reads
+// base + voff + soff, lane i writes lds_addr + 16 i.  Inline asm for the same
+// reason as dma16.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_buf(uint32_t voff, i32x4 rsrc, int soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Copy plan of one wavefront for a ring stage of the BM + BN row tile (A rows
+// then B rows): copy i of wavefront w fills 16-row segment 4i + w; lane l
+// copies row 16 seg + l/4, 16-byte piece (l%4) ^ swz16(l/4) of the 64-byte
+// chunk, so the slot holds swizzled rows.  Rows past M / N repeat the last
+// row.  Whole chunks are copied by buffer loads from a per-segment SGPR
+// descriptor with the chunk offset in a scalar register (no vector
+// instruction per copy; row strides <= 2^24 keep 15 rows + K below 2^31);
+// a partial last chunk (K % 64 != 0) takes guarded global copies that read
+// zeros past K.
+template <int DPS, int BM>
+struct DmaPlan {
+  const uint8_t* src[DPS];
+  int koff[DPS];
+  i32x4 rs[DPS];
+  uint32_t vo[DPS];
+
+  __device__ __forceinline__ void init(const uint8_t* A, int64_t lda, const uint8_t* B,
+                                       int64_t ldb, int m0, int n0, int M, int N, int w,
+                                       int lane) {
+#pragma unroll
+    for (int i = 0; i < DPS; ++i) {
+      const int seg = i * 4 + w;
+      const int r = lane >> 2;
+      koff[i] = ((lane & 3) ^ swz16(r)) * 16;
+      const bool isa = seg * 16 < BM;
+      const uint8_t* base = isa ? A : B;
+      const int64_t ld = isa ? lda : ldb;
+      const int first = isa ? m0 + seg * 16 : n0 + seg * 16 - BM;
+      const int last = (isa ? M : N) - 1;
+      const int r0 = min(first, last), rr = min(first + r, last);
+      src[i] = base + (int64_t)rr * ld + koff[i];
+      rs[i] = sgpr_rsrc(base + (int64_t)r0 * ld);
+      vo[i] = (uint32_t)((int64_t)(rr - r0) * ld) + (uint32_t)koff[i];
+    }
+  }
+
+  // copies of the chunk at byte offset kb into the slot at LDS address slot
+  __device__ __forceinline__ void issue(uint32_t slot, int kb, int K, int w) const {
+    if (kb + kChunk <= K) {
+#pragma unroll
+      for (int i = 0; i < DPS; ++i) dma16_buf(vo[i], rs[i], kb, slot + (uint32_t)((i * 4 + w) * 1024));
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPS; ++i) {
+        const void* p = kb + koff[i] < K ? (const void*)(src[i] + kb) : (const void*)g_zero16;
+        dma16(p, slot + (uint32_t)((i * 4 + w) * 1024));
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Rowwise tile kernel: BM x BN workgroup tile, 4 wavefronts in a 2 x 2 grid
 // (wave tile BM/2 x BN/2), 64-wide K chunks in an NSLOT-slot LDS ring filled
@@ -300,29 +378,11 @@ __global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
   const int g = lane >> 4, r16 = lane & 15;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
 
-  // DMA sources: instruction i of wave w fills segment i*4+w of a slot; lane
-  // l writes row (segment*16 + l/4), position l%4, which holds chunk
-  // (l%4) ^ swz16(l/4).
-  const uint8_t* src[DPS];
-  int koff[DPS];
-#pragma unroll
-  for (int i = 0; i < DPS; ++i) {
-    const int seg = i * 4 + w;
-    const int row = seg * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swz16(lane >> 2);
-    koff[i] = c * 16;
-    src[i] = row < BM ? A + (int64_t)min(m0 + row, M - 1) * lda + koff[i]
-                      : B + (int64_t)min(n0 + row - BM, N - 1) * ldb + koff[i];
-  }
+  DmaPlan<DPS, BM> dma;
+  dma.init(A, lda, B, ldb, m0, n0, M, N, w, lane);
   const int nkc = (K + kChunk - 1) / kChunk;
   auto issue = [&](int kc) {
-    const uint32_t slot = lds0 + (uint32_t)((kc % NSLOT) * SLOT);
-    const int64_t kb = (int64_t)kc * kChunk;
-#pragma unroll
-    for (int i = 0; i < DPS; ++i) {
-      const void* p = kb + koff[i] < K ? (const void*)(src[i] + kb) : (const void*)g_zero16;
-      dma16(p, slot + (uint32_t)((i * 4 + w) * 1024));
-    }
+    dma.issue(lds0 + (uint32_t)((kc % NSLOT) * SLOT), kc * kChunk, K, w);
   };
 
   // fragment read offsets (bytes within a slot)
@@ -421,27 +481,12 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
   const int wm = w >> 1, wn = w & 1;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
 
-  const uint8_t* src[DPS];
-  int koff[DPS];
-#pragma unroll
-  for (int i = 0; i < DPS; ++i) {
-    const int seg = i * 4 + w;
-    const int row = seg * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swz16(lane >> 2);
-    koff[i] = c * 16;
-    src[i] = row < BM ? A + (int64_t)min(m0 + row, M - 1) * lda + koff[i]
-                      : B + (int64_t)min(n0 + row - BM, N - 1) * ldb + koff[i];
-  }
+  DmaPlan<DPS, BM> dma;
+  dma.init(A, lda, B, ldb, m0, n0, M, N, w, lane);
   const int nkc = (K + kChunk - 1) / kChunk;
   const int nkb = (K + 127) / 128;
   auto issue = [&](int kc) {
-    const uint32_t slot = lds0 + (uint32_t)((kc % NSLOT) * SLOT);
-    const int64_t kb = (int64_t)kc * kChunk;
-#pragma unroll
-    for (int i = 0; i < DPS; ++i) {
-      const void* p = kb + koff[i] < K ? (const void*)(src[i] + kb) : (const void*)g_zero16;
-      dma16(p, slot + (uint32_t)((i * 4 + w) * 1024));
-    }
+    dma.issue(lds0 + (uint32_t)((kc % NSLOT) * SLOT), kc * kChunk, K, w);
   };
   // scale bytes of K blocks kb0 .. kb0 + SEGB - 1 for the tile's rows: thread t
   // copies half a row (32 blocks); rows past M repeat row M - 1

@@ -175,7 +175,8 @@ fp8sm_status fp8sm_quant_weight_block128(const void* w, fp8sm_dtype in, int64_t 
  * alignment, K % 16, and bf16 output rows N % 8): K % 16 == 0, lda, ldb % 16
  * == 0, A, B 16-byte aligned; N % 8 == 0, ldc % 8 == 0, C 16-byte aligned;
  * M, N >= 0 (0: nothing launched); K >= 0 (K == 0 writes zeros);
- * K <= 65536.  Violations return an error status; there is no fallback path.
+ * K <= 65536; lda, ldb <= 2^24 bytes (ERR_RANGE beyond).  Violations return
+ * an error status; there is no fallback path.
  */
 fp8sm_status fp8sm_scaled_mm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                              void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
