@@ -68,6 +68,9 @@ def test_scaled_mm_rejects_bad_arguments_before_any_launch():
     assert _mm(lib, C=0) == E["ERR_NULL"]
     assert _mm(lib, A=8) == E["ERR_ALIGN"]                    # 16-byte rule
     assert _mm(lib, K=1 << 17, lda=1 << 17, ldb=1 << 17) == E["ERR_RANGE"]
+    # row strides beyond 2^24 bytes: 32-bit operand offsets over a 64-row panel
+    assert _mm(lib, lda=(1 << 24) + 16) == E["ERR_RANGE"]
+    assert _mm(lib, ldb=(1 << 24) + 16) == E["ERR_RANGE"]
     assert _mm(lib, M=0) == E["OK"]                           # empty: nothing launched
     assert _mm(lib, N=0, ldc=8) == E["OK"]
 

@@ -127,6 +127,36 @@ def test_padded_leading_dimensions():
         assert torch.all(Cb[:, N:] == 3.0), fp8sm.variant_name(v)
 
 
+@pytest.mark.parametrize("M", [9, 70])
+def test_largest_row_strides_every_variant(M):
+    # lda = ldb = 2^24 bytes, the largest the call accepts: 32-bit operand
+    # offsets over a whole panel stay in range; K = 80 runs one whole chunk
+    # (buffer copies) and a 16-byte tail (guarded copies)
+    N, K, ld = 72, 80, 1 << 24
+    A, B, sa, sb = _quantized_case(M, N, K, seed=97)
+    Af = torch.zeros((M - 1) * ld + K, dtype=torch.uint8, device=cuda())
+    Bf = torch.zeros((N - 1) * ld + K, dtype=torch.uint8, device=cuda())
+    Ag = torch.as_strided(Af, (M, K), (ld, 1))
+    Bg = torch.as_strided(Bf, (N, K), (ld, 1))
+    Ag.copy_(torch.from_numpy(A).to(cuda()))
+    Bg.copy_(torch.from_numpy(B).to(cuda()))
+    sag, sbg = to_gpu_f32(sa), to_gpu_f32(sb)
+    res = og.scaled_mm(A, B, sa, sb)
+    first = None
+    for v in _variants_for(M):
+        prev = fp8sm.force_variant(v)
+        try:
+            c = fp8sm.scaled_mm(Ag, Bg, sag, sbg, ROW, COL)
+            torch.cuda.synchronize()
+        finally:
+            fp8sm.force_variant(prev)
+        bits = bf16_bits(c)
+        assert_within_tolerance(bits, res, K, f"ld 2^24 {fp8sm.variant_name(v)} M={M}")
+        if first is None:
+            first = bits
+        assert np.array_equal(bits, first), fp8sm.variant_name(v)
+
+
 @pytest.mark.parametrize("shape", [(37, 264, 80), (100, 136, 208), (16, 48, 1552),
                                    (257, 128, 4096)])
 @pytest.mark.parametrize("out,with_bias", [("fp16", False), ("bf16", True), ("fp16", True)])
