@@ -124,7 +124,8 @@ __device__ __forceinline__ bf16x8 widen_step(const Frag32& f, float scale) {
   return widen_e4m3_x8(d0, d1);
 }
 
-template <int TM, int TN, bool SCALED, int S>
+// FRESH: the step starts a new partial (C = +0 instead of the accumulator).
+template <int TM, int TN, bool SCALED, int S, bool FRESH = false>
 __device__ __forceinline__ void mma32_step(const Frag32 (&fa)[TM], const float (&asc)[TM],
                                            const Frag32 (&fb)[TN], f32x16 (&acc)[TM][TN]) {
   bf16x8 a[TM], b[TN];
@@ -132,20 +133,22 @@ __device__ __forceinline__ void mma32_step(const Frag32 (&fa)[TM], const float (
   for (int i = 0; i < TM; ++i) a[i] = widen_step<SCALED, S>(fa[i], asc[i]);
 #pragma unroll
   for (int j = 0; j < TN; ++j) b[j] = widen_step<false, S>(fb[j], 1.0f);
+  const f32x16 zero = {};
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], FRESH ? zero : acc[i][j], 0, 0, 0);
 }
 
 // With SCALED, A row subtile i is widened times asc[i], a power of two: the
 // widen is exact (every finite E4M3 value times 2^e, |e| <= 100, is a bf16
 // value), so products and fp32 sums are the unscaled ones times 2^e.
-template <int TM, int TN, bool SCALED>
+// FRESH: the chunk opens a K block, whose partial starts from zero.
+template <int TM, int TN, bool SCALED, bool FRESH = false>
 __device__ __forceinline__ void mma32_chunk(const Frag32 (&fa)[TM], const float (&asc)[TM],
                                             const Frag32 (&fb)[TN], f32x16 (&acc)[TM][TN]) {
-  mma32_step<TM, TN, SCALED, 0>(fa, asc, fb, acc);
+  mma32_step<TM, TN, SCALED, 0, FRESH>(fa, asc, fb, acc);
   mma32_step<TM, TN, SCALED, 1>(fa, asc, fb, acc);
   mma32_step<TM, TN, SCALED, 2>(fa, asc, fb, acc);
   mma32_step<TM, TN, SCALED, 3>(fa, asc, fb, acc);
@@ -534,7 +537,11 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 
   for (int c = 0; c < NSLOT - 1 && c < nkc; ++c) issue(c);
   stage_scales(0);  // visible after the first loop barrier
-  for (int kc = 0; kc < nkc; ++kc) {
+  // one chunk: wait for its copies, barrier, queue the copies NSLOT - 1
+  // chunks ahead, read the fragments, multiply (FRESH: the chunk opens a K
+  // block and its partial starts from zero, so no register clearing is needed
+  // after a promotion)
+  auto chunk = [&](int kc, auto fresh) {
     const int after = min(NSLOT - 2, nkc - 1 - kc);
     if (after >= 2)
       wait_vmcnt<2 * DPS>();
@@ -543,8 +550,8 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
     else
       wait_vmcnt<0>();
     __syncthreads();  // chunk kc visible to all; slot of chunk kc-1 free
-    const int kb = kc >> 1;
-    if ((kc & 1) == 0) {
+    if constexpr (decltype(fresh)::value) {
+      const int kb = kc >> 1;
       if (kb > 0 && kb % SEGB == 0) {  // every wavefront is past the previous segment
         stage_scales(kb);
         __syncthreads();
@@ -567,18 +574,19 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
       fb[j].q[0] = *reinterpret_cast<const uint4*>(slot + b_off0 + j * 32 * kChunk);
       fb[j].q[1] = *reinterpret_cast<const uint4*>(slot + b_off1 + j * 32 * kChunk);
     }
-    mma32_chunk<TM, TN, true>(fa, asc, fb, acc);
-    if ((kc & 1) || kc == nkc - 1) {  // end of a K block: promote its partial
+    mma32_chunk<TM, TN, true, decltype(fresh)::value>(fa, asc, fb, acc);
+  };
+  // one K block (two chunks; the last block of a K tail may have one) per
+  // iteration, then its partial is promoted into the fp64 master
+  for (int kc = 0; kc < nkc; kc += 2) {
+    chunk(kc, std::true_type{});
+    if (kc + 1 < nkc) chunk(kc + 1, std::false_type{});
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            mast[i][j][v] = fma((double)acc[i][j][v], sbk, mast[i][j][v]);
-            acc[i][j][v] = 0.f;
-          }
-    }
+        for (int v = 0; v < 16; ++v) mast[i][j][v] = fma((double)acc[i][j][v], sbk, mast[i][j][v]);
   }
 
 #pragma unroll
