@@ -120,10 +120,13 @@ def _time_launches(fn, reps, nrot, stream, batches=3):
 
     fn(i) launches on input set i % nrot; with nrot > 1 the sets together
     exceed the 256 MB last-level cache, so every launch reads from HBM.
-    Each batch is queued behind a device read sized to outlast the host's
-    enqueueing (measured during warm-up), so the HIP events around the batch
-    see no host gaps; a batch whose enqueue still outlasted that read is
-    flagged.  Returns (median batch mean, host_bound)."""
+    Two measurements of the same launch sequence:
+      * graph: the `reps` launches captured once in a HIP graph and replayed
+        (no host work between launches); HIP events around each replay;
+      * queued: each batch enqueued behind a device read sized to outlast the
+        host's enqueueing (measured during warm-up); a batch whose enqueue
+        still outlasted that read is flagged host-bound.
+    Returns (median graph mean, median queued mean, host_bound)."""
     import torch
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -152,7 +155,21 @@ def _time_launches(fn, reps, nrot, stream, batches=3):
             host_bound = True
         means.append(a.elapsed_time(b) * 1e3 / reps)
     del spacer
-    return sorted(means)[len(means) // 2], host_bound
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(reps):
+            fn(i)
+    gmeans = []
+    for _ in range(batches):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        gmeans.append(a.elapsed_time(b) * 1e3 / reps)
+    del g
+    return sorted(gmeans)[len(gmeans) // 2], sorted(means)[len(means) // 2], host_bound
 
 
 def _rotations(bytes_per_set, cold):
@@ -168,7 +185,13 @@ def suite(reps):
     import torch
     from column_scaled_gemm_amd import fp8sm, inputs
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
+    # a stream of its own (default priority) so launch sequences can be captured
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        return _suite_rows(reps, stream, np, torch, fp8sm, inputs, dev)
+
+
+def _suite_rows(reps, stream, np, torch, fp8sm, inputs, dev):
     out = []
 
     def emit(row, **kv):
@@ -187,22 +210,22 @@ def suite(reps):
         del w
         qas = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nrot)]
         sas = [torch.empty((M, 1), dtype=torch.float32, device=dev) for _ in range(nrot)]
-        us_q, hb = _time_launches(
+        us_q, qus_q, hb = _time_launches(
             lambda i: fp8sm.quant_group(xs[i % nrot], -1, q=qas[i % nrot], scales=sas[i % nrot],
                                         stream=stream), max(reps, nrot), nrot, stream)
         qbytes = 2 * M * K + M * K + 4 * M
-        emit("a1 per-token quant", workload=f"{name} bf16[{M},{K}]", us=round(us_q, 2),
+        emit("a1 per-token quant", workload=f"{name} bf16[{M},{K}]", us=round(us_q, 2), us_queued=round(qus_q, 2),
              GBps=round(qbytes / us_q / 1e3, 1), hbm_frac=round(qbytes / us_q / 1e3 / PEAK_HBM, 3),
              cache="cold", host_bound=hb)
         qa, sa = qas[0], sas[0]
         del xs, qas[1:], sas[1:]
         c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        us_g, hb = _time_launches(
+        us_g, qus_g, hb = _time_launches(
             lambda i: fp8sm.scaled_mm(qa, qb, sa.reshape(-1), sb.reshape(-1), fp8sm.KIND_ROW,
                                       fp8sm.KIND_COL, c=c, stream=stream),
             max(3, reps // 2), 1, stream, batches=2)
         tf = 2.0 * M * N * K / us_g / 1e6
-        emit("a5 rowwise GEMM", workload=f"{name} {M}x{K}x{N}", us=round(us_g, 1),
+        emit("a5 rowwise GEMM", workload=f"{name} {M}x{K}x{N}", us=round(us_g, 1), us_queued=round(qus_g, 1),
              TFLOPs=round(tf, 1), bf16_peak_frac=round(tf / PEAK_BF16_MFMA, 4),
              fp8_peak_frac=round(tf / PEAK_FP8_MFMA, 4), cache="warm",
              variant=fp8sm.variant_name(fp8sm.pick_variant(M, N, K)))
@@ -222,17 +245,17 @@ def suite(reps):
         for M in inputs.DECODE_MS:
             qx = torch.empty((M, Kd), dtype=torch.uint8, device=dev)
             cs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(nrot)]
-            us_s, hb_s = _time_launches(lambda i: fp8sm.quant_static(x[:M], xsc, q=qx, stream=stream),
+            us_s, qus_s, hb_s = _time_launches(lambda i: fp8sm.quant_static(x[:M], xsc, q=qx, stream=stream),
                                         max(reps, 20), 1, stream)
-            us_d, hb = _time_launches(
+            us_d, qus_d, hb = _time_launches(
                 lambda i: fp8sm.scaled_mm(qx, qws[i % nrot], xsc, ws, fp8sm.KIND_TENSOR,
                                           fp8sm.KIND_TENSOR, c=cs[i % nrot], stream=stream),
                 max(reps, nrot), nrot, stream)
             byts = N * Kd + M * Kd + 2 * M * N
-            emit("a3 static quant", workload=f"bf16[{M},{Kd}]", us=round(us_s, 2), cache="warm",
+            emit("a3 static quant", workload=f"bf16[{M},{Kd}]", us=round(us_s, 2), us_queued=round(qus_s, 2), cache="warm",
                  host_bound=hb_s)
             emit("a6 decode GEMM", workload=f"M={M} K={Kd} N={N} per-tensor",
-                 us=round(us_d, 2), GBps=round(byts / us_d / 1e3, 1),
+                 us=round(us_d, 2), us_queued=round(qus_d, 2), GBps=round(byts / us_d / 1e3, 1),
                  hbm_frac=round(byts / us_d / 1e3 / PEAK_HBM, 3),
                  TFLOPs=round(2.0 * M * N * Kd / us_d / 1e6, 2), cache="cold", host_bound=hb,
                  variant=fp8sm.variant_name(fp8sm.pick_variant(M, N, Kd)))
@@ -248,23 +271,23 @@ def suite(reps):
         xgs = [xin.to(dev) for _ in range(nrot)]
         qas = [torch.empty((Mf, Kf), dtype=torch.uint8, device=dev) for _ in range(nrot)]
         eas = [torch.empty((Mf, Kf // 128), dtype=torch.uint8, device=dev) for _ in range(nrot)]
-        us_f, hb = _time_launches(
+        us_f, qus_f, hb = _time_launches(
             lambda i: fp8sm.quant_group(xgs[i % nrot], 128, fp8sm.SCALE_UE8M0_BYTE,
                                         fuse_silu_mul=True, q=qas[i % nrot], scales=eas[i % nrot],
                                         stream=stream), max(reps, nrot), nrot, stream)
         fbytes = 4 * Mf * Kf + Mf * Kf + Mf * Kf // 128
         emit("a4 fused SiLU-mul + 1x128 UE8M0 quant", workload=f"{tag}[{Mf},{2 * Kf}]",
-             us=round(us_f, 2), GBps=round(fbytes / us_f / 1e3, 1),
+             us=round(us_f, 2), us_queued=round(qus_f, 2), GBps=round(fbytes / us_f / 1e3, 1),
              hbm_frac=round(fbytes / us_f / 1e3 / PEAK_HBM, 3), cache="cold", host_bound=hb)
         qa, ea = qas[0], eas[0]
         del xgs, qas, eas
         c = torch.empty((Mf, Nf), dtype=torch.bfloat16, device=dev)
-        us_b, hb = _time_launches(
+        us_b, qus_b, hb = _time_launches(
             lambda i: fp8sm.scaled_mm(qa, qb, ea, sbb, fp8sm.KIND_GROUP128_UE8M0,
                                       fp8sm.KIND_BLOCK128, c=c, stream=stream),
             max(reps, 5), 1, stream, batches=2)
         tf = 2.0 * Mf * Nf * Kf / us_b / 1e6
-        emit("a7 blockwise GEMM", workload=f"{tag} {Mf}x{Kf}x{Nf}", us=round(us_b, 1),
+        emit("a7 blockwise GEMM", workload=f"{tag} {Mf}x{Kf}x{Nf}", us=round(us_b, 1), us_queued=round(qus_b, 1),
              TFLOPs=round(tf, 1), bf16_peak_frac=round(tf / PEAK_BF16_MFMA, 4), cache="warm")
         del qa, ea, c
         torch.cuda.empty_cache()
@@ -279,13 +302,13 @@ def suite(reps):
     gus = [mo.gu.to(dev) for _ in range(nrot)]
     q = torch.empty((E, Tm, I), dtype=torch.uint8, device=dev)
     es = torch.empty((E, Tm, I // 128), dtype=torch.uint8, device=dev)
-    us_m, hb = _time_launches(
+    us_m, qus_m, hb = _time_launches(
         lambda i: fp8sm.quant_group_batched(gus[i % nrot], 128, fp8sm.SCALE_UE8M0_BYTE,
                                             fuse_silu_mul=True, rows=rows, q=q, scales=es,
                                             stream=stream), max(reps, nrot), nrot, stream)
     mbytes = live * (4 * I + I + I // 128)
     emit("f2 masked fused SiLU-mul + 1x128 UE8M0 quant",
-         workload=f"bf16[{E},{Tm},{2 * I}] {live} live rows", us=round(us_m, 2),
+         workload=f"bf16[{E},{Tm},{2 * I}] {live} live rows", us=round(us_m, 2), us_queued=round(qus_m, 2),
          GBps=round(mbytes / us_m / 1e3, 1), hbm_frac=round(mbytes / us_m / 1e3 / PEAK_HBM, 3),
          cache="cold", host_bound=hb)
     del gus
@@ -300,7 +323,7 @@ def suite(reps):
         wss.append(ws)
     del mo
     c = torch.empty((E, Tm, H), dtype=torch.bfloat16, device=dev)
-    us_e, hb = _time_launches(
+    us_e, qus_e, hb = _time_launches(
         lambda i: fp8sm.scaled_mm_batched(q, wqs[i % nrot], es, wss[i % nrot],
                                           fp8sm.KIND_GROUP128_UE8M0, fp8sm.KIND_BLOCK128,
                                           rows=rows, c=c, stream=stream),
@@ -309,7 +332,7 @@ def suite(reps):
               + live * H * 2)
     emit("f2 masked grouped blockwise GEMM",
          workload=f"{E} experts x {Tm}-row slabs, {live} live rows, K={I} N={H}",
-         us=round(us_e, 1), GBps=round(ebytes / us_e / 1e3, 1),
+         us=round(us_e, 1), us_queued=round(qus_e, 1), GBps=round(ebytes / us_e / 1e3, 1),
          hbm_frac=round(ebytes / us_e / 1e3 / PEAK_HBM, 3),
          TFLOPs=round(2.0 * live * H * I / us_e / 1e6, 1), cache="cold", host_bound=hb)
     del wqs, wss, q, es, c
@@ -328,13 +351,13 @@ def suite(reps):
             for _ in range(nrot)]
     qs_ = [torch.empty((Rs, Ks), dtype=torch.uint8, device=dev) for _ in range(nrot)]
     ss_ = torch.empty((Ks // 128, Rs), dtype=torch.uint8, device=dev)
-    us_sc, hb = _time_launches(
+    us_sc, qus_sc, hb = _time_launches(
         lambda i: fp8sm.quant_group_scatter(xs_[i % nrot], dsts[i % nrot], Rs, q=qs_[i % nrot],
                                             scales=ss_, stream=stream),
         max(reps, nrot), nrot, stream)
     scb = 2 * Ts * Ks + Rs * Ks + Rs * (Ks // 128) + 4 * Rs
     emit("f3 scatter 1x128 UE8M0 quant", workload=f"bf16[{Ts},{Ks}] top-{topk} -> {Rs} rows",
-         us=round(us_sc, 2), GBps=round(scb / us_sc / 1e3, 1),
+         us=round(us_sc, 2), us_queued=round(qus_sc, 2), GBps=round(scb / us_sc / 1e3, 1),
          hbm_frac=round(scb / us_sc / 1e3 / PEAK_HBM, 3), cache="cold", host_bound=hb)
     del xs_, dsts, qs_, ss_
     torch.cuda.empty_cache()
@@ -350,12 +373,12 @@ def suite(reps):
     ps = torch.tensor([0.011, 0.017, 0.013], dtype=torch.float32, device=dev)
     wq = torch.empty((Nq, Kq), dtype=torch.uint8, device=dev)
     ms = torch.empty(1, dtype=torch.float32, device=dev)
-    us_r, hb = _time_launches(
+    us_r, qus_r, hb = _time_launches(
         lambda i: fp8sm.requantize_max_scale(wcs[i % nrot], ps, widths, q=wq, max_scale=ms,
                                              stream=stream), max(reps, nrot), nrot, stream)
     rbytes = 2 * Nq * Kq
     emit("f4 requantize fused weight to the max scale", workload=f"qkv weight [{Nq},{Kq}], 3 partitions",
-         us=round(us_r, 1), GBps=round(rbytes / us_r / 1e3, 1),
+         us=round(us_r, 1), us_queued=round(qus_r, 1), GBps=round(rbytes / us_r / 1e3, 1),
          hbm_frac=round(rbytes / us_r / 1e3 / PEAK_HBM, 3), cache="cold", host_bound=hb)
     del wcs, wq
     torch.cuda.empty_cache()
