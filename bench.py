@@ -387,16 +387,17 @@ def _suite_rows(reps, stream, np, torch, fp8sm, inputs, dev):
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library "
+              "has no multi-GPU path; the GEMM's column-parallel sharding needs no exchange "
+              "and would scale per GPU.", file=sys.stderr)
+        sys.exit(2)
     if args.suite:
         suite(max(args.steps, 5))
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU path is not part of this build.", file=sys.stderr)
-        sys.exit(2)
     import numpy as np
     import torch
     from column_scaled_gemm_amd import fp8sm, inputs
