@@ -170,12 +170,15 @@ __device__ __forceinline__ float rowwise_epilogue(float acc, float sa, float sb)
 // the final rounding: out = rnd(RN32(RN32(acc * sa) * sb) + bias).
 enum { EPI_F16 = 1, EPI_BIAS = 2 };
 
+// Both conversions are the hardware's round-to-nearest-even (overflow to
+// +-inf); the bf16 one (v_cvt_pk_bf16_f32) equals f32_to_bf16_rne for every
+// fp32 value that is not NaN (checked over all 2^32 patterns on gfx950).
 template <int EPI>
 __device__ __forceinline__ uint16_t epi_round(float v) {
   if constexpr ((EPI & EPI_F16) != 0)
-    return __builtin_bit_cast(uint16_t, (_Float16)v);  // RNE, overflow to inf
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
   else
-    return f32_to_bf16_rne(v);
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
 template <int EPI>
@@ -198,12 +201,17 @@ __device__ __forceinline__ void store_row4(uint16_t* __restrict__ C, int64_t ldc
                                            const f32x4& acc, float sar,
                                            const float* __restrict__ sb, int sb_vec,
                                            const uint16_t* __restrict__ bias) {
-  uint16_t o[4];
+  float y[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    o[v] = epi_round<EPI>(epi_value<EPI>(acc[v], sar, sb[sb_vec ? c + v : 0], bias, c + v));
-  const uint32_t lo = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-  const uint32_t hi = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+  for (int v = 0; v < 4; ++v) y[v] = epi_value<EPI>(acc[v], sar, sb[sb_vec ? c + v : 0], bias, c + v);
+  uint32_t lo, hi;
+  if constexpr ((EPI & EPI_F16) != 0) {
+    lo = (uint32_t)epi_round<EPI>(y[0]) | ((uint32_t)epi_round<EPI>(y[1]) << 16);
+    hi = (uint32_t)epi_round<EPI>(y[2]) | ((uint32_t)epi_round<EPI>(y[3]) << 16);
+  } else {  // two values per conversion instruction
+    lo = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)y[0], (__bf16)y[1]});
+    hi = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)y[2], (__bf16)y[3]});
+  }
   *reinterpret_cast<uint2*>(C + (int64_t)r * ldc + c) = make_uint2(lo, hi);
 }
 
