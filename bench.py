@@ -34,8 +34,8 @@ PEAK_HBM = 8000.0           # GB/s
 # passes, scaled by a plain-copy calibration (profiles/
 # gemm_rowwise_128x256_qkv_traffic.md).  Valid only for the gemm.hip source it
 # was measured on; reported as null once that file changes.
-TRAFFIC = {"gemm_src_sha256_prefix": "2237b854fc3f8c64", "workload": "qkv",
-           "kernel": "tile128x256", "bytes": 1724.2e6 + 358.6e6}
+TRAFFIC = {"gemm_src_sha256_prefix": "a73bf551d04ce3b2", "workload": "qkv",
+           "kernel": "tile128x256", "bytes": 1717.9e6 + 358.3e6}
 
 
 def measured_traffic(workload, variant):
