@@ -328,6 +328,12 @@ int fp8sm_force_variant(int id) {
   return g_forced_variant.exchange(id);
 }
 
+int fp8sm_variant_accepts(int id, int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  (void)K;  // no variant bounds N or K beyond the call's own limits
+  return id >= 0 && id < VAR_COUNT && variant_accepts(id, M) ? 1 : 0;
+}
+
 int fp8sm_pick_variant(int64_t M, int64_t N, int64_t K) {
   const int forced = g_forced_variant.load();
   if (forced >= 0) return forced;

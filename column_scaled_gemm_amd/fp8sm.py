@@ -53,6 +53,7 @@ SIGNATURES = {
     "fp8sm_variant_count": (_int, []),
     "fp8sm_variant_name": (ctypes.c_char_p, [_int]),
     "fp8sm_pick_variant": (_int, [_i64, _i64, _i64]),
+    "fp8sm_variant_accepts": (_int, [_int, _i64, _i64, _i64]),
 }
 
 _lib = None
@@ -130,6 +131,11 @@ def variant_name(vid):
 
 def pick_variant(M, N, K):
     return _load().fp8sm_pick_variant(M, N, K)
+
+
+def variant_accepts(vid, M, N, K):
+    """Whether kernel variant vid computes an M x N x K rowwise call."""
+    return bool(_load().fp8sm_variant_accepts(vid, M, N, K))
 
 
 # ---------------------------------------------------------------- tensor calls

@@ -249,6 +249,19 @@ def test_variant_table_routes_decode_shapes_by_m():
     assert fp8sm.pick_variant(8320, 21504, 5376) == fp8sm.pick_variant(8320, 21504, 5376)
 
 
+def test_variant_accepts_bounds_decode_variants_by_m():
+    from column_scaled_gemm_amd import fp8sm
+    names = {fp8sm.variant_name(v): v for v in range(fp8sm.variant_count())}
+    for name, cap in (("decode16", 16), ("decode32", 32), ("decode64", 64)):
+        v = names[name]
+        assert fp8sm.variant_accepts(v, cap, 4096, 65536)
+        assert not fp8sm.variant_accepts(v, cap + 1, 4096, 4096)
+    for name in ("tile128x256", "tile128x128", "tile256x128", "tile256x256"):
+        assert fp8sm.variant_accepts(names[name], 1 << 20, 16, 65536)
+    assert not fp8sm.variant_accepts(-1, 1, 1, 16)
+    assert not fp8sm.variant_accepts(fp8sm.variant_count(), 1, 1, 16)
+
+
 def test_binding_rejects_views_with_a_strided_last_dimension():
     # the C ABI takes one row stride; a view whose elements are not contiguous
     # within a row must not reach it (checked before any call)

@@ -20,13 +20,9 @@ SENT_U8 = 0x5A
 SENT_U16 = 0x7FC1   # a NaN pattern in bf16 and in fp16: no kernel writes it
 
 
-def _variants_for(M):
-    out = []
-    for v in range(fp8sm.variant_count()):
-        cap = {"decode16": 16, "decode32": 32, "decode64": 64}.get(fp8sm.variant_name(v), 1 << 30)
-        if M <= cap:
-            out.append(v)
-    return out
+def _variants_for(M, K):
+    """Every rowwise kernel variant that computes an M-row call with this K."""
+    return [v for v in range(fp8sm.variant_count()) if fp8sm.variant_accepts(v, M, 0, K)]
 
 
 def _strided_3d(t, B, M, pad_rows=1, pad_cols=64, dtype=None):
@@ -189,7 +185,7 @@ def test_batched_rowwise_strided_every_variant(shape, per_b):
     sbd = torch.from_numpy(sb).to(cuda())
     res = ob.scaled_mm_batched(A, W, sa, sb if per_b else np.stack([sb] * B))
     first = None
-    for v in _variants_for(M):
+    for v in _variants_for(M, K):
         prev = fp8sm.force_variant(v)
         try:
             c = fp8sm.scaled_mm_batched(av, wd, sad, sbd, ROW, COL)
@@ -215,7 +211,7 @@ def test_masked_rowwise_with_bias_leaves_dead_rows(out):
     bias = torch.from_numpy(r.standard_normal(N).astype(F32)).to(tdt)
     res = ob.scaled_mm_batched(A, W, sa, sb, rows=rows, bias=bias.float().numpy(), out=out)
     av = _a_view(A)
-    for v in _variants_for(M):
+    for v in _variants_for(M, K):
         prev = fp8sm.force_variant(v)
         try:
             c = torch.full((B, M, N), SENT_U16, dtype=torch.int16, device=cuda()).view(tdt)

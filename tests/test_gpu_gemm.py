@@ -20,14 +20,9 @@ def _mm(a, b, sa, sb, ka=ROW, kb=COL):
     return bf16_bits(c)
 
 
-def _variants_for(M):
-    names = []
-    for v in range(fp8sm.variant_count()):
-        n = fp8sm.variant_name(v)
-        cap = {"decode16": 16, "decode32": 32, "decode64": 64}.get(n, 1 << 30)
-        if M <= cap:
-            names.append(v)
-    return names
+def _variants_for(M, K):
+    """Every rowwise kernel variant that computes an M-row call with this K."""
+    return [v for v in range(fp8sm.variant_count()) if fp8sm.variant_accepts(v, M, 0, K)]
 
 
 def _mm_variant(v, *args, **kw):
@@ -46,7 +41,7 @@ def test_one_hot_products_of_all_finite_codes_are_exact():
         B = np.zeros((n, K), np.uint8)
         A[:, kpos] = c
         B[:254, kpos] = c
-        for v in _variants_for(254):
+        for v in _variants_for(254, K):
             got = _mm_variant(v, A, B, F32(1), F32(1), T, T)
             want = og.scaled_mm(A, B, 1.0, 1.0).bits
             assert np.array_equal(got, want), (kpos, fp8sm.variant_name(v))
@@ -61,7 +56,7 @@ def test_small_integer_sums_are_exact():
     A = codes[r.integers(0, 33, (70, 1024))]
     B = codes[r.integers(0, 33, (136, 1024))]
     want = og.scaled_mm(A, B, 1.0, 1.0).bits
-    for v in _variants_for(70):
+    for v in _variants_for(70, 1024):
         assert np.array_equal(_mm_variant(v, A, B, np.ones(70, F32), np.ones(136, F32)), want), v
 
 
@@ -94,7 +89,7 @@ def test_ragged_shapes_every_variant_bitwise_equal_and_within_bound(shape):
     A, B, sa, sb = _quantized_case(M, N, K, seed=M + N + K)
     res = og.scaled_mm(A, B, sa, sb)
     outs = {}
-    for v in _variants_for(M):
+    for v in _variants_for(M, K):
         outs[v] = _mm_variant(v, A, B, sa, sb)
         assert_within_tolerance(outs[v], res, K, f"{shape} {fp8sm.variant_name(v)}")
     first = next(iter(outs.values()))
@@ -113,7 +108,7 @@ def test_padded_leading_dimensions():
     Bb[:, :K] = torch.from_numpy(B)
     Ag, Bg = Ab.to(cuda())[:, :K], Bb.to(cuda())[:, :K]
     sag, sbg = to_gpu_f32(sa), to_gpu_f32(sb)
-    for v in _variants_for(M):
+    for v in _variants_for(M, K):
         prev = fp8sm.force_variant(v)
         try:
             Cb = torch.full((M, N + 8), 3.0, dtype=torch.bfloat16, device=cuda())
@@ -143,7 +138,7 @@ def test_largest_row_strides_every_variant(M):
     sag, sbg = to_gpu_f32(sa), to_gpu_f32(sb)
     res = og.scaled_mm(A, B, sa, sb)
     first = None
-    for v in _variants_for(M):
+    for v in _variants_for(M, K):
         prev = fp8sm.force_variant(v)
         try:
             c = fp8sm.scaled_mm(Ag, Bg, sag, sbg, ROW, COL)
@@ -177,7 +172,7 @@ def test_bias_and_fp16_epilogues_every_variant(shape, out, with_bias):
         bias_t = bias_t.to(cuda())
     res = og.scaled_mm(A, B, sa, sb, bias=bias_v, out=out)
     outs = {}
-    for v in _variants_for(M):
+    for v in _variants_for(M, K):
         prev = fp8sm.force_variant(v)
         try:
             c = fp8sm.scaled_mm(to_gpu_u8(A), to_gpu_u8(B), to_gpu_f32(sa), to_gpu_f32(sb),
@@ -203,7 +198,7 @@ def test_fp16_output_overflow_and_k0_bias():
     B = np.full((N, K), big, np.uint8)
     sb = np.full(N, 1.0, F32)
     sb[8:] = 2.0 ** -10                                  # 64 * 448^2 / 1024 = 12544: finite
-    for v in _variants_for(M):
+    for v in _variants_for(M, K):
         prev = fp8sm.force_variant(v)
         try:
             c = fp8sm.scaled_mm(to_gpu_u8(A), to_gpu_u8(B), to_gpu_f32(np.ones(M, F32)),
@@ -409,7 +404,7 @@ def test_max_k_rowwise_every_variant():
     A, B, sa, sb = _quantized_case(M, N, K, seed=5)
     res = og.scaled_mm(A, B, sa, sb)
     outs = {}
-    for v in _variants_for(M):
+    for v in _variants_for(M, K):
         outs[v] = _mm_variant(v, A, B, sa, sb)
         assert_within_tolerance(outs[v], res, K, f"max K {fp8sm.variant_name(v)}")
     first = next(iter(outs.values()))
