@@ -20,6 +20,14 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 8-byte streaming store (nontemporal), used by the 1x128 group quants:
+// measured 2.5-4% faster on the fused SiLU-mul quant and 11% on the scattered
+// quant; the per-token kernels measured slower with it and keep plain stores.
+__device__ __forceinline__ void store_stream8(void* p, const uint2 v) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
+
 // Exact widening of eight packed 16-bit inputs (one 16-byte load) to fp32.
 template <bool F16>
 __device__ __forceinline__ void widen8(const uint4 v, float* f) {

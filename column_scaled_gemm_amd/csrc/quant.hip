@@ -116,7 +116,7 @@ __device__ __forceinline__ void quant_group128(float* y, int l16, int64_t row, i
   int eb;
   const uint2 codes = group128_codes<FMT>(y, &sval, &eb);
   if (row >= 0) {
-    *reinterpret_cast<uint2*>(q + row * ld_q + grp * 128 + l16 * 8) = codes;
+    store_stream8(q + row * ld_q + grp * 128 + l16 * 8, codes);
     if (l16 == 0) {
       const int64_t idx = mn_major ? grp * mpad + row : row * G + grp;
       store_scale<FMT>(scales, idx, sval, eb);
@@ -140,7 +140,7 @@ __device__ __forceinline__ void quant_group128_o32(float* y, int l16, bool valid
   if (valid) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = y[i] * mult;
-    *reinterpret_cast<uint2*>(q + qo) = to_e4m3_x8(y);
+    store_stream8(q + qo, to_e4m3_x8(y));
     if (l16 == 0) store_scale<FMT>(scales, so, sval, eb);
   }
 }
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void quant_g128_scatter_kernel(
     for (int j = 0; j < topk; ++j) {
       const int64_t d = dl[j];
       if (d < 0 || d >= R) continue;
-      *reinterpret_cast<uint2*>(q + d * ld_q + grp[u] * 128 + l16 * 8) = codes;
+      store_stream8(q + d * ld_q + grp[u] * 128 + l16 * 8, codes);
       if (l16 == 0) store_scale<FMT>(scales, mn_major ? grp[u] * rpad + d : d * G + grp[u], sval, eb);
     }
   }
