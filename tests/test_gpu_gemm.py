@@ -428,3 +428,61 @@ def test_blockwise_ue8m0_long_k_restages_scales(shape):
     torch.cuda.synchronize()
     a_vals = np.exp2(e.astype(np.float64) - 127).astype(F32)
     assert_within_tolerance(bf16_bits(c), og.blockwise_mm(A, a_vals, B, sb), K, f"long K {shape}")
+
+
+@pytest.mark.parametrize("M,variant", [(12, None), (300, None), (300, "tile128x256")])
+def test_quant_and_rowwise_gemm_graph_replays(M, variant):
+    # the hot path's step (per-token quant of the activations, rowwise GEMM
+    # against per-channel weights) captured once in a HIP graph and replayed
+    # with new activations, eager work and synchronizations between replays:
+    # every replay equals the eager step bitwise and the oracle (codes
+    # bit-exact, GEMM within the bound); K = 1040 has a 16-byte K tail
+    N, K = 520, 1040
+    print(f"[case] graph replay M={M} variant={variant}", flush=True)
+    r = inputs.rng(M + 7)
+    w = inputs.to_dtype(r.standard_normal((N, K), dtype=np.float32) * F32(0.02))
+    xs = [inputs.to_dtype(r.standard_normal((M, K), dtype=np.float32)) for _ in range(3)]
+    qb, sb = fp8sm.quant_group(w.to(cuda()), -1)
+    ob = oq.quant_group(inputs.widen(w), K)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=cuda())
+    qa = torch.empty((M, K), dtype=torch.uint8, device=cuda())
+    sa = torch.empty((M, 1), dtype=torch.float32, device=cuda())
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=cuda())
+    names = {fp8sm.variant_name(v): v for v in range(fp8sm.variant_count())}
+    prev = fp8sm.force_variant(names[variant] if variant else -1)
+    try:
+        def step():
+            fp8sm.quant_group(x, -1, q=qa, scales=sa)
+            fp8sm.scaled_mm(qa, qb, sa.reshape(-1), sb.reshape(-1), ROW, COL, c=c)
+
+        x.copy_(xs[0].to(cuda()))
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step()                        # warm up outside capture
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        for xi in xs + xs[:1]:
+            x.copy_(xi.to(cuda()))
+            for t in (qa, sa, c):
+                t.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            qg, sg, cg = qa.clone(), sa.clone(), bf16_bits(c)
+            for t in (qa, sa, c):
+                t.zero_()
+            step()
+            torch.cuda.synchronize()
+            assert torch.equal(qa, qg) and torch.equal(sa, sg)
+            assert np.array_equal(bf16_bits(c), cg)
+            oa = oq.quant_group(inputs.widen(xi), K)
+            assert np.array_equal(qg.cpu().numpy(), oa.codes)
+            res = og.scaled_mm(oa.codes, ob.codes, oa.scale.reshape(-1), ob.scale.reshape(-1))
+            assert_within_tolerance(cg, res, K, f"graph replay M={M} {variant}")
+    finally:
+        fp8sm.force_variant(prev)
