@@ -30,7 +30,7 @@ def f32_bits(t):
 
 
 def tolerance_report(gpu_bits, res, K):
-    """North-star GEMM bound: |gpu - oracle| <= 2^-7 |oracle| + 1e-3 sa sb sqrt(K).
+    """GEMM accuracy bound: |gpu - oracle| <= 2^-7 |oracle| + 1e-3 sa sb sqrt(K).
 
     The GPU bits are decoded in the oracle result's output dtype (bf16 or
     fp16); equal values, infinities included, count as no error.

@@ -1,5 +1,5 @@
 """GPU parity of the scaled GEMMs against the oracle: bit-exact where the
-result is exactly representable, the benchmark spec's bound elsewhere, and bitwise
+result is exactly representable, the accuracy bound 2^-7|ref| + 1e-3 sa sb sqrt(K) elsewhere, and bitwise
 row invariance across M and across kernel variants."""
 import numpy as np
 import pytest
