@@ -767,6 +767,21 @@ static unsigned persistent_blocks(int64_t work_per_block_units, int64_t units, i
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(need, share));
 }
 
+// Rows walked by `per_block` rows at a time per workgroup: when the last round
+// of rows would be less than half full, keep the number of rounds but spread
+// the rows evenly over fewer workgroups, so that round is not run by a few
+// workgroups alone (8320 rows on 4096 persistent wavefronts would leave 128
+// rows as a third round: 26.0 -> 24.9 us measured).  A fuller last round
+// keeps the whole grid, whose extra rows in flight are worth more.
+static unsigned balanced_blocks(unsigned blocks, int64_t rows, int64_t per_block) {
+  const int64_t units = (int64_t)blocks * per_block;
+  const int64_t tail = rows % units;
+  if (tail == 0 || 2 * tail >= units) return blocks;
+  const int64_t rounds = std::max<int64_t>(1, (rows + units - 1) / units);
+  const int64_t need = (rows + rounds - 1) / rounds;  // rows per round
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, (need + per_block - 1) / per_block));
+}
+
 static dim3 grid2(int64_t blocks, const QuantBatch& bt) {
   return dim3((unsigned)blocks, (unsigned)bt.count);
 }
@@ -845,7 +860,8 @@ static hipError_t launch_token_nc(int fmt, const QuantArgs& a, hipStream_t s) {
     constexpr int FMT = decltype(f)::value;
     static std::atomic<int> occ{0};
     const int per_cu = resident_blocks(quant_token_kernel<F16, NC, NFULL, FMT>, occ);
-    const int64_t blocks = persistent_blocks(4, a.M, a.batch.count, (int64_t)per_cu * cu_count());
+    const int64_t blocks = balanced_blocks(
+        persistent_blocks(4, a.M, a.batch.count, (int64_t)per_cu * cu_count()), a.M, 4);
     hipLaunchKernelGGL((quant_token_kernel<F16, NC, NFULL, FMT>), grid2(blocks, a.batch),
                        dim3(256), 0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.batch);
   });
@@ -879,7 +895,8 @@ static hipError_t launch_token_wg(int fmt, const QuantArgs& a, hipStream_t s) {
     constexpr int FMT = decltype(f)::value;
     static std::atomic<int> occ{0};
     const int per_cu = resident_blocks(quant_token_wg_kernel<F16, NCW, FMT>, occ);
-    const int64_t blocks = persistent_blocks(1, a.M, a.batch.count, (int64_t)per_cu * cu_count());
+    const int64_t blocks = balanced_blocks(
+        persistent_blocks(1, a.M, a.batch.count, (int64_t)per_cu * cu_count()), a.M, 1);
     hipLaunchKernelGGL((quant_token_wg_kernel<F16, NCW, FMT>), grid2(blocks, a.batch), dim3(256),
                        0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.batch);
   });
