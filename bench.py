@@ -181,17 +181,18 @@ def suite(reps):
     """One JSON line per hot-path row.  Quant and decode rows are cold (each
     launch reads its inputs from HBM); the rowwise and blockwise GEMMs, which
     are compute-bound, are warm."""
+    import torch
+    # a stream of its own (default priority) so launch sequences can be captured
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        return _suite_rows(reps, stream)
+
+
+def _suite_rows(reps, stream):
     import numpy as np
     import torch
     from column_scaled_gemm_amd import fp8sm, inputs
     dev = torch.device("cuda:0")
-    # a stream of its own (default priority) so launch sequences can be captured
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        return _suite_rows(reps, stream, np, torch, fp8sm, inputs, dev)
-
-
-def _suite_rows(reps, stream, np, torch, fp8sm, inputs, dev):
     out = []
 
     def emit(row, **kv):
