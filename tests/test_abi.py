@@ -247,6 +247,17 @@ def test_variant_table_routes_decode_shapes_by_m():
     finally:
         fp8sm.force_variant(prev)
     assert fp8sm.pick_variant(8320, 21504, 5376) == fp8sm.pick_variant(8320, 21504, 5376)
+    # the measured choices: 128x256 tiles on the H3 shapes, the register-streamed
+    # decode kernel for the decode batches, the M <= 64 decode kernel for the
+    # 64-row tiny case
+    pick = lambda M, N, K: fp8sm.variant_name(fp8sm.pick_variant(M, N, K))  # noqa: E731
+    for shape in ((8320, 21504, 5376), (23216, 28672, 5376), (15760, 28672, 5376),
+                  (8320, 5376, 14336)):
+        assert pick(*shape) == "tile128x256", shape
+    for M in (1, 4, 16):
+        for N in (4096, 14336):
+            assert pick(M, N, 4096) == "decode16", (M, N)
+    assert pick(64, 256, 512) == "decode64"
 
 
 def test_variant_accepts_bounds_decode_variants_by_m():
