@@ -160,9 +160,9 @@ def quant_group(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul
     if scales is None:
         dt = torch.uint8 if fmt == SCALE_UE8M0_BYTE else torch.float32
         scales = torch.empty(scale_shape(fmt, layout, M, K_out, group), dtype=dt, device=x.device)
-    st = _load().fp8sm_quant_group(_ptr(x), _dtype_code(x), M, K_out, x.stride(0), group,
+    st = _load().fp8sm_quant_group(_ptr(x), _dtype_code(x), M, K_out, _ld(x), group,
                                    FUSE_SILU_MUL if fuse_silu_mul else 0, fmt, layout,
-                                   _ptr(q), q.stride(0), _ptr(scales), _stream(stream))
+                                   _ptr(q), _ld(q), _ptr(scales), _stream(stream))
     _check(st, "fp8sm_quant_group")
     return q, scales
 
@@ -174,8 +174,8 @@ def quant_static(x, scale, q=None, stream=None):
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     _unit_last(q, "q")
-    st = _load().fp8sm_quant_static(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(scale),
-                                    _ptr(q), q.stride(0), _stream(stream))
+    st = _load().fp8sm_quant_static(_ptr(x), _dtype_code(x), M, K, _ld(x), _ptr(scale),
+                                    _ptr(q), _ld(q), _stream(stream))
     _check(st, "fp8sm_quant_static")
     return q
 
@@ -189,8 +189,8 @@ def quant_weight_block128(w, q=None, scales=None, stream=None):
     if scales is None:
         scales = torch.empty(((N + 127) // 128, (K + 127) // 128), dtype=torch.float32,
                              device=w.device)
-    st = _load().fp8sm_quant_weight_block128(_ptr(w), _dtype_code(w), N, K, w.stride(0), _ptr(q),
-                                             q.stride(0), _ptr(scales), _stream(stream))
+    st = _load().fp8sm_quant_weight_block128(_ptr(w), _dtype_code(w), N, K, _ld(w), _ptr(q),
+                                             _ld(q), _ptr(scales), _stream(stream))
     _check(st, "fp8sm_quant_weight_block128")
     return q, scales
 
@@ -203,8 +203,8 @@ def silu_mul_f32(x, y=None, stream=None):
     if y is None:
         y = torch.empty((M, K), dtype=torch.float32, device=x.device)
     _unit_last(y, "y")
-    st = _load().fp8sm_silu_mul_f32(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(y),
-                                    y.stride(0), _stream(stream))
+    st = _load().fp8sm_silu_mul_f32(_ptr(x), _dtype_code(x), M, K, _ld(x), _ptr(y),
+                                    _ld(y), _stream(stream))
     _check(st, "fp8sm_silu_mul_f32")
     return y
 
@@ -225,15 +225,15 @@ def scaled_mm(a, b, sa, sb, kind_a, kind_b, c=None, M=None, stream=None, bias=No
         c = torch.empty((M, N), dtype=out_dtype, device=b.device)
     _unit_last(c, "c")
     if bias is None and out_dtype == torch.bfloat16:
-        st = _load().fp8sm_scaled_mm(_ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(c),
-                                     c.stride(0), M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb),
+        st = _load().fp8sm_scaled_mm(_ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(c),
+                                     _ld(c), M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb),
                                      _stream(stream))
         _check(st, "fp8sm_scaled_mm")
         return c
     out = {torch.bfloat16: BF16, torch.float16: FP16}[out_dtype]
     if c.dtype != out_dtype or (bias is not None and bias.dtype != out_dtype):
         raise TypeError("fp8sm_scaled_mm_ex: c and bias must have the output dtype")
-    st = _load().fp8sm_scaled_mm_ex(_ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(c), c.stride(0),
+    st = _load().fp8sm_scaled_mm_ex(_ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(c), _ld(c),
                                     M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb),
                                     None if bias is None else _ptr(bias), out, _stream(stream))
     _check(st, "fp8sm_scaled_mm_ex")
@@ -254,6 +254,22 @@ def _rows_arg(rows, B):
 def _unit_last(t, what):
     if t.stride(-1) != 1:
         raise ValueError(f"{what}: the last dimension must be contiguous")
+
+
+def _ld(t):
+    """Row stride in elements of a matrix (or of a batch's rows).  A tensor
+    with no elements addresses no memory, and torch reports arbitrary strides
+    for it (1 for a zero-width matrix): pass the smallest row stride the
+    layout rules accept instead, the row length rounded up to 16."""
+    if t.numel() == 0:
+        return -(-t.shape[-1] // 16) * 16
+    return t.stride(-2)
+
+
+def _bs(t, B):
+    """Batch stride in elements of a 3-D operand: 0 for one batch or for a
+    tensor with no elements (which addresses no memory)."""
+    return t.stride(0) if B > 1 and t.numel() else 0
 
 
 def quant_group_batched(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul=False,
@@ -278,9 +294,9 @@ def quant_group_batched(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_
         raise ValueError("scales must be contiguous with room for every batch")
     rows = _rows_arg(rows, B)
     st = _load().fp8sm_quant_group_batched(
-        _ptr(x), _dtype_code(x), B, M, K_out, x.stride(0) if B > 1 else 0, x.stride(1), _ptr(rows),
+        _ptr(x), _dtype_code(x), B, M, K_out, _bs(x, B), _ld(x), _ptr(rows),
         group, FUSE_SILU_MUL if fuse_silu_mul else 0, fmt, layout, _ptr(q),
-        q.stride(0) if B > 1 else 0, q.stride(1), _ptr(scales), _stream(stream))
+        _bs(q, B), _ld(q), _ptr(scales), _stream(stream))
     _check(st, "fp8sm_quant_group_batched")
     return q, scales
 
@@ -293,8 +309,8 @@ def quant_static_batched(x, scale, q=None, stream=None):
         q = torch.empty((B, M, K), dtype=torch.uint8, device=x.device)
     _unit_last(q, "q")
     st = _load().fp8sm_quant_static_batched(
-        _ptr(x), _dtype_code(x), B, M, K, x.stride(0) if B > 1 else 0, x.stride(1), _ptr(scale),
-        _ptr(q), q.stride(0) if B > 1 else 0, q.stride(1), _stream(stream))
+        _ptr(x), _dtype_code(x), B, M, K, _bs(x, B), _ld(x), _ptr(scale),
+        _ptr(q), _bs(q, B), _ld(q), _stream(stream))
     _check(st, "fp8sm_quant_static_batched")
     return q
 
@@ -335,10 +351,10 @@ def scaled_mm_batched(a, b, sa, sb, kind_a, kind_b, rows=None, c=None, bias=None
     if b.dim() == 3:
         if b.shape[0] != B:
             raise ValueError("a per-batch weight needs one [N, K] slab per batch")
-        N, bs_b = b.shape[1], (b.stride(0) if B > 1 else 0)
-        ldb = b.stride(1)
+        N, bs_b = b.shape[1], _bs(b, B)
+        ldb = _ld(b)
     else:
-        N, bs_b, ldb = b.shape[0], 0, b.stride(0)
+        N, bs_b, ldb = b.shape[0], 0, _ld(b)
     if out_dtype is None:
         out_dtype = c.dtype if c is not None else torch.bfloat16
     if c is None:
@@ -355,8 +371,8 @@ def scaled_mm_batched(a, b, sa, sb, kind_a, kind_b, rows=None, c=None, bias=None
     out = {torch.bfloat16: BF16, torch.float16: FP16}[out_dtype]
     rows = _rows_arg(rows, B)
     st = _load().fp8sm_scaled_mm_batched(
-        B, _ptr(rows), _ptr(a), a.stride(0) if B > 1 else 0, a.stride(1), _ptr(b), bs_b, ldb,
-        _ptr(c), c.stride(0) if B > 1 else 0, c.stride(1), M, N, K, kind_a, _ptr(sa), bs_sa, kind_b,
+        B, _ptr(rows), _ptr(a), _bs(a, B), _ld(a), _ptr(b), bs_b, ldb,
+        _ptr(c), _bs(c, B), _ld(c), M, N, K, kind_a, _ptr(sa), bs_sa, kind_b,
         _ptr(sb), bs_sb, None if bias is None else _ptr(bias), out, _stream(stream))
     _check(st, "fp8sm_scaled_mm_batched")
     return c
@@ -380,8 +396,8 @@ def requantize_max_scale(w, scales, widths, q=None, max_scale=None, stream=None)
     if max_scale is None:
         max_scale = torch.empty(1, dtype=torch.float32, device=w.device)
     arr, n = _widths_arg(widths)
-    st = _load().fp8sm_requantize_max_scale(_ptr(w), w.stride(0), N, K, arr, n, _ptr(scales),
-                                            _ptr(q), q.stride(0), _ptr(max_scale),
+    st = _load().fp8sm_requantize_max_scale(_ptr(w), _ld(w), N, K, arr, n, _ptr(scales),
+                                            _ptr(q), _ld(q), _ptr(max_scale),
                                             _stream(stream))
     _check(st, "fp8sm_requantize_max_scale")
     return max_scale, q
@@ -413,8 +429,8 @@ def quant_group_scatter(x, dst, R, fmt=SCALE_UE8M0_BYTE, layout=LAYOUT_MN_MAJOR,
         scales = torch.empty(scale_shape(fmt, layout, R, K, 128), dtype=dt, device=x.device)
     if scales.numel() * scales.element_size() < scale_bytes(fmt, layout, R, K, 128):
         raise ValueError("scales too small")
-    st = _load().fp8sm_quant_group_scatter(_ptr(x), _dtype_code(x), T, K, x.stride(0), _ptr(dst),
-                                           dst.shape[1], R, fmt, layout, _ptr(q), q.stride(0),
+    st = _load().fp8sm_quant_group_scatter(_ptr(x), _dtype_code(x), T, K, _ld(x), _ptr(dst),
+                                           dst.shape[1], R, fmt, layout, _ptr(q), _ld(q),
                                            _ptr(scales), _stream(stream))
     _check(st, "fp8sm_quant_group_scatter")
     return q, scales
