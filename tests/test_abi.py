@@ -287,3 +287,22 @@ def test_binding_rejects_views_with_a_strided_last_dimension():
                  lambda: fp8sm.quant_group_batched(x[None], 128)):
         with pytest.raises(ValueError):
             call()
+
+
+def test_binding_strides_of_empty_tensors_satisfy_the_layout_rules():
+    # torch gives a zero-width matrix a row stride of 1; the binding passes the
+    # smallest stride the ABI accepts for a tensor with no elements (row length
+    # rounded up to 16) and a zero batch stride, and the tensor's own strides
+    # otherwise
+    import torch
+    from column_scaled_gemm_amd import fp8sm
+    assert torch.empty((64, 0)).stride(0) == 1
+    assert fp8sm._ld(torch.empty((64, 0))) == 0
+    assert fp8sm._ld(torch.empty((0, 512))) == 512
+    assert fp8sm._ld(torch.empty((0, 500))) == 512
+    assert fp8sm._ld(torch.empty((3, 64, 0))) == 0
+    assert fp8sm._bs(torch.empty((3, 64, 0)), 3) == 0
+    assert fp8sm._bs(torch.empty((3, 0, 512)), 3) == 0
+    x = torch.empty((3, 10, 256))[:, 1:9, :128]
+    assert fp8sm._ld(x) == 256 and fp8sm._bs(x, 3) == 2560 and fp8sm._bs(x, 1) == 0
+    assert fp8sm._ld(torch.empty((5, 48))) == 48
