@@ -257,11 +257,12 @@ def _unit_last(t, what):
 
 
 def _ld(t):
-    """Row stride in elements of a matrix (or of a batch's rows).  A tensor
-    with no elements addresses no memory, and torch reports arbitrary strides
-    for it (1 for a zero-width matrix): pass the smallest row stride the
-    layout rules accept instead, the row length rounded up to 16."""
-    if t.numel() == 0:
+    """Row stride in elements of a matrix (or of a batch's rows).  With no
+    elements, or one row per batch, the stride addresses nothing beyond row 0,
+    and torch may report any value for it (1 for a zero-width matrix or a
+    transposed column): pass the smallest row stride the layout rules accept
+    instead, the row length rounded up to 16."""
+    if t.numel() == 0 or t.shape[-2] == 1:
         return -(-t.shape[-1] // 16) * 16
     return t.stride(-2)
 

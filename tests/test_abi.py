@@ -291,9 +291,9 @@ def test_binding_rejects_views_with_a_strided_last_dimension():
 
 def test_binding_strides_of_empty_tensors_satisfy_the_layout_rules():
     # torch gives a zero-width matrix a row stride of 1; the binding passes the
-    # smallest stride the ABI accepts for a tensor with no elements (row length
-    # rounded up to 16) and a zero batch stride, and the tensor's own strides
-    # otherwise
+    # smallest stride the ABI accepts for a tensor with no elements or a single
+    # row (row length rounded up to 16), a zero batch stride for an empty
+    # tensor, and the tensor's own strides otherwise
     import torch
     from column_scaled_gemm_amd import fp8sm
     assert torch.empty((64, 0)).stride(0) == 1
@@ -306,3 +306,8 @@ def test_binding_strides_of_empty_tensors_satisfy_the_layout_rules():
     x = torch.empty((3, 10, 256))[:, 1:9, :128]
     assert fp8sm._ld(x) == 256 and fp8sm._bs(x, 3) == 2560 and fp8sm._bs(x, 1) == 0
     assert fp8sm._ld(torch.empty((5, 48))) == 48
+    # one row: only row 0 is addressed, whatever torch reports as its stride
+    col_t = torch.empty((512, 1)).T
+    assert col_t.shape == (1, 512) and col_t.stride(0) == 1
+    assert fp8sm._ld(col_t) == 512
+    assert fp8sm._ld(torch.empty((4, 1, 100))) == 112
