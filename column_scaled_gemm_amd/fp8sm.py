@@ -157,9 +157,11 @@ def quant_group(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul
     if q is None:
         q = torch.empty((M, K_out), dtype=torch.uint8, device=x.device)
     _unit_last(q, "q")
+    _holds(q, (M, K_out), "q", torch.uint8)
     if scales is None:
-        dt = torch.uint8 if fmt == SCALE_UE8M0_BYTE else torch.float32
-        scales = torch.empty(scale_shape(fmt, layout, M, K_out, group), dtype=dt, device=x.device)
+        scales = torch.empty(scale_shape(fmt, layout, M, K_out, group), dtype=_scale_dtype(fmt),
+                             device=x.device)
+    _holds_bytes(scales, scale_bytes(fmt, layout, M, K_out, group), "scales", _scale_dtype(fmt))
     st = _load().fp8sm_quant_group(_ptr(x), _dtype_code(x), M, K_out, _ld(x), group,
                                    FUSE_SILU_MUL if fuse_silu_mul else 0, fmt, layout,
                                    _ptr(q), _ld(q), _ptr(scales), _stream(stream))
@@ -174,6 +176,8 @@ def quant_static(x, scale, q=None, stream=None):
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     _unit_last(q, "q")
+    _holds(q, (M, K), "q", torch.uint8)
+    _holds_bytes(scale, 4, "scale", torch.float32)
     st = _load().fp8sm_quant_static(_ptr(x), _dtype_code(x), M, K, _ld(x), _ptr(scale),
                                     _ptr(q), _ld(q), _stream(stream))
     _check(st, "fp8sm_quant_static")
@@ -186,9 +190,11 @@ def quant_weight_block128(w, q=None, scales=None, stream=None):
     if q is None:
         q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     _unit_last(q, "q")
+    _holds(q, (N, K), "q", torch.uint8)
     if scales is None:
         scales = torch.empty(((N + 127) // 128, (K + 127) // 128), dtype=torch.float32,
                              device=w.device)
+    _holds_bytes(scales, 4 * ((N + 127) // 128) * ((K + 127) // 128), "scales", torch.float32)
     st = _load().fp8sm_quant_weight_block128(_ptr(w), _dtype_code(w), N, K, _ld(w), _ptr(q),
                                              _ld(q), _ptr(scales), _stream(stream))
     _check(st, "fp8sm_quant_weight_block128")
@@ -203,6 +209,7 @@ def silu_mul_f32(x, y=None, stream=None):
     if y is None:
         y = torch.empty((M, K), dtype=torch.float32, device=x.device)
     _unit_last(y, "y")
+    _holds(y, (M, K), "y", torch.float32)
     st = _load().fp8sm_silu_mul_f32(_ptr(x), _dtype_code(x), M, K, _ld(x), _ptr(y),
                                     _ld(y), _stream(stream))
     _check(st, "fp8sm_silu_mul_f32")
@@ -224,6 +231,13 @@ def scaled_mm(a, b, sa, sb, kind_a, kind_b, c=None, M=None, stream=None, bias=No
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=b.device)
     _unit_last(c, "c")
+    _holds(a, (M, K), "a", torch.uint8)
+    _holds(b, (N, K), "b", torch.uint8)
+    _holds(c, (M, N), "c")
+    _holds_scale(sa, kind_a, M, N, K, "sa")
+    _holds_scale(sb, kind_b, M, N, K, "sb")
+    if bias is not None:
+        _holds_bytes(bias, 2 * N, "bias")
     if bias is None and out_dtype == torch.bfloat16:
         st = _load().fp8sm_scaled_mm(_ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(c),
                                      _ld(c), M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb),
@@ -273,6 +287,43 @@ def _bs(t, B):
     return t.stride(0) if B > 1 and t.numel() else 0
 
 
+def _holds(t, shape, what, dtype=None):
+    """The C ABI cannot see buffer sizes: a tensor the caller supplies must
+    span at least `shape` (dimension by dimension) and have the dtype the
+    call reads or writes, checked here before any call."""
+    if t.dim() != len(shape) or any(have < need for have, need in zip(t.shape, shape)):
+        raise ValueError(f"{what}: needs shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: needs dtype {dtype}, got {t.dtype}")
+
+
+def _holds_bytes(t, nbytes, what, dtype=None):
+    """A flat buffer the caller supplies (scales) must be contiguous and hold
+    `nbytes` bytes."""
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: needs dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what}: needs {nbytes} contiguous bytes")
+
+
+def _scale_dtype(fmt):
+    return torch.uint8 if fmt == SCALE_UE8M0_BYTE else torch.float32
+
+
+def _holds_scale(t, kind, M, N, K, what):
+    """A GEMM scale operand holds its kind's elements (bytes for
+    GROUP128_UE8M0, fp32 otherwise; unknown kinds are left to the ABI)."""
+    G = (K + 127) // 128
+    elems = {KIND_TENSOR: 1, KIND_ROW: M, KIND_COL: N, KIND_GROUP128_UE8M0: M * G,
+             KIND_GROUP128_FP32: M * G, KIND_BLOCK128: ((N + 127) // 128) * G}.get(kind)
+    if elems is None:
+        return
+    if kind == KIND_GROUP128_UE8M0:
+        _holds_bytes(t, elems, what, torch.uint8)
+    else:
+        _holds_bytes(t, 4 * elems, what, torch.float32)
+
+
 def quant_group_batched(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul=False,
                         rows=None, q=None, scales=None, stream=None):
     """x [B, M, K_in] bf16/fp16 with any batch / row strides (unit element
@@ -290,6 +341,9 @@ def quant_group_batched(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_
         scales = torch.empty((B,) + scale_shape(fmt, layout, M, K_out, group), dtype=dt,
                              device=x.device)
     _unit_last(q, "q")
+    _holds(q, (B, M, K_out), "q", torch.uint8)
+    if scales.dtype != _scale_dtype(fmt):
+        raise TypeError(f"scales: needs dtype {_scale_dtype(fmt)}, got {scales.dtype}")
     per = scale_bytes(fmt, layout, M, K_out, group)
     if not scales.is_contiguous() or scales.numel() * scales.element_size() < B * per:
         raise ValueError("scales must be contiguous with room for every batch")
@@ -309,6 +363,8 @@ def quant_static_batched(x, scale, q=None, stream=None):
     if q is None:
         q = torch.empty((B, M, K), dtype=torch.uint8, device=x.device)
     _unit_last(q, "q")
+    _holds(q, (B, M, K), "q", torch.uint8)
+    _holds_bytes(scale, 4, "scale", torch.float32)
     st = _load().fp8sm_quant_static_batched(
         _ptr(x), _dtype_code(x), B, M, K, _bs(x, B), _ld(x), _ptr(scale),
         _ptr(q), _bs(q, B), _ld(q), _stream(stream))
@@ -361,6 +417,9 @@ def scaled_mm_batched(a, b, sa, sb, kind_a, kind_b, rows=None, c=None, bias=None
     if c is None:
         c = torch.empty((B, M, N), dtype=out_dtype, device=a.device)
     _unit_last(c, "c")
+    _holds(a, (B, M, K), "a", torch.uint8)
+    _holds(b, (B, N, K) if b.dim() == 3 else (N, K), "b", torch.uint8)
+    _holds(c, (B, M, N), "c")
     if c.dtype != out_dtype or (bias is not None and bias.dtype != out_dtype):
         raise TypeError("c and bias must have the output dtype")
     G = (K + 127) // 128
@@ -396,6 +455,10 @@ def requantize_max_scale(w, scales, widths, q=None, max_scale=None, stream=None)
         q = torch.empty_like(w)
     if max_scale is None:
         max_scale = torch.empty(1, dtype=torch.float32, device=w.device)
+    _holds(w, (N, K), "w", torch.uint8)
+    _holds(q, (N, K), "q", torch.uint8)
+    _holds_bytes(scales, 4 * len(widths), "scales", torch.float32)
+    _holds_bytes(max_scale, 4, "max_scale", torch.float32)
     arr, n = _widths_arg(widths)
     st = _load().fp8sm_requantize_max_scale(_ptr(w), _ld(w), N, K, arr, n, _ptr(scales),
                                             _ptr(q), _ld(q), _ptr(max_scale),
@@ -409,6 +472,8 @@ def scales_to_channelwise(scales, widths, out=None, stream=None):
     arr, n = _widths_arg(widths)
     if out is None:
         out = torch.empty(int(sum(widths)), dtype=torch.float32, device=scales.device)
+    _holds_bytes(scales, 4 * len(widths), "scales", torch.float32)
+    _holds_bytes(out, 4 * int(sum(widths)), "out", torch.float32)
     st = _load().fp8sm_scales_to_channelwise(_ptr(scales), arr, n, _ptr(out), _stream(stream))
     _check(st, "fp8sm_scales_to_channelwise")
     return out
@@ -425,11 +490,12 @@ def quant_group_scatter(x, dst, R, fmt=SCALE_UE8M0_BYTE, layout=LAYOUT_MN_MAJOR,
         raise ValueError("dst must be a contiguous int32 [T, topk] tensor")
     if q is None:
         q = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+    _unit_last(q, "q")
+    _holds(q, (R, K), "q", torch.uint8)
     if scales is None:
-        dt = torch.uint8 if fmt == SCALE_UE8M0_BYTE else torch.float32
-        scales = torch.empty(scale_shape(fmt, layout, R, K, 128), dtype=dt, device=x.device)
-    if scales.numel() * scales.element_size() < scale_bytes(fmt, layout, R, K, 128):
-        raise ValueError("scales too small")
+        scales = torch.empty(scale_shape(fmt, layout, R, K, 128), dtype=_scale_dtype(fmt),
+                             device=x.device)
+    _holds_bytes(scales, scale_bytes(fmt, layout, R, K, 128), "scales", _scale_dtype(fmt))
     st = _load().fp8sm_quant_group_scatter(_ptr(x), _dtype_code(x), T, K, _ld(x), _ptr(dst),
                                            dst.shape[1], R, fmt, layout, _ptr(q), _ld(q),
                                            _ptr(scales), _stream(stream))

@@ -311,3 +311,55 @@ def test_binding_strides_of_empty_tensors_satisfy_the_layout_rules():
     assert col_t.shape == (1, 512) and col_t.stride(0) == 1
     assert fp8sm._ld(col_t) == 512
     assert fp8sm._ld(torch.empty((4, 1, 100))) == 112
+
+
+def test_binding_rejects_outputs_and_operands_too_small_before_any_call():
+    # the C ABI cannot see buffer sizes: every caller-supplied tensor is checked
+    # against what the call reads or writes (host tensors: a check that let a
+    # call through would fail on the stream lookup, not with these errors)
+    import torch
+    from column_scaled_gemm_amd import fp8sm
+    ROW, COL, U8, BF = fp8sm.KIND_ROW, fp8sm.KIND_COL, torch.uint8, torch.bfloat16
+    x = torch.zeros(8, 256, dtype=BF)
+    codes = torch.zeros(8, 256, dtype=U8)
+    w = torch.zeros(16, 256, dtype=U8)
+
+    def ones(n):
+        return torch.ones(n)
+
+    cases = [
+        (ValueError, lambda: fp8sm.quant_group(x, 128, fuse_silu_mul=True, q=torch.zeros(8, 64, dtype=U8))),
+        (ValueError, lambda: fp8sm.quant_group(x, 128, q=codes, scales=torch.zeros(8, 1))),
+        (TypeError, lambda: fp8sm.quant_group(x, 128, fp8sm.SCALE_UE8M0_BYTE, q=codes,
+                                              scales=torch.zeros(8, 2))),
+        (TypeError, lambda: fp8sm.quant_group(x, 128, q=torch.zeros(8, 256, dtype=torch.int8))),
+        (ValueError, lambda: fp8sm.quant_static(x, ones(1), q=codes[:4])),
+        (ValueError, lambda: fp8sm.quant_weight_block128(x, scales=torch.zeros(1))),
+        (ValueError, lambda: fp8sm.silu_mul_f32(x, y=torch.zeros(8, 64))),
+        (ValueError, lambda: fp8sm.scaled_mm(codes, w, ones(8), ones(16), ROW, COL,
+                                             c=torch.zeros(8, 8, dtype=BF))),
+        (ValueError, lambda: fp8sm.scaled_mm(codes, w[:, :128], ones(8), ones(16), ROW, COL)),
+        (ValueError, lambda: fp8sm.scaled_mm(codes, w, ones(4), ones(16), ROW, COL)),
+        (ValueError, lambda: fp8sm.scaled_mm(codes, w, ones(8), ones(8), ROW, COL)),
+        (TypeError, lambda: fp8sm.scaled_mm(codes, w, ones(8).double(), ones(16), ROW, COL)),
+        (ValueError, lambda: fp8sm.scaled_mm(codes, w, ones(8), ones(16), ROW, COL, M=9)),
+        (ValueError, lambda: fp8sm.scaled_mm(codes, w, torch.zeros(8, 1, dtype=U8), ones(2),
+                                             fp8sm.KIND_GROUP128_UE8M0, fp8sm.KIND_BLOCK128)),
+        (ValueError, lambda: fp8sm.quant_group_batched(x[None], 128,
+                                                       q=torch.zeros(1, 4, 256, dtype=U8))),
+        (ValueError, lambda: fp8sm.quant_static_batched(x[None], ones(1),
+                                                        q=torch.zeros(1, 8, 128, dtype=U8))),
+        (ValueError, lambda: fp8sm.scaled_mm_batched(codes[None], w, ones(8), ones(16), ROW, COL,
+                                                     c=torch.zeros(1, 8, 8, dtype=BF))),
+        (ValueError, lambda: fp8sm.scaled_mm_batched(codes[None], w[:, :64], ones(8), ones(16),
+                                                     ROW, COL)),
+        (ValueError, lambda: fp8sm.requantize_max_scale(w, ones(1), [16],
+                                                        q=torch.zeros(8, 256, dtype=U8))),
+        (ValueError, lambda: fp8sm.requantize_max_scale(w, ones(1), [8, 8])),
+        (ValueError, lambda: fp8sm.scales_to_channelwise(ones(2), [8, 8], out=torch.zeros(15))),
+        (ValueError, lambda: fp8sm.quant_group_scatter(x, torch.zeros(8, 2, dtype=torch.int32), 16,
+                                                       q=torch.zeros(8, 256, dtype=U8))),
+    ]
+    for i, (err, call) in enumerate(cases):
+        with pytest.raises(err):
+            call()
