@@ -422,6 +422,8 @@ def scaled_mm_batched(a, b, sa, sb, kind_a, kind_b, rows=None, c=None, bias=None
     _holds(c, (B, M, N), "c")
     if c.dtype != out_dtype or (bias is not None and bias.dtype != out_dtype):
         raise TypeError("c and bias must have the output dtype")
+    if bias is not None:
+        _holds_bytes(bias, 2 * N, "bias")
     G = (K + 127) // 128
     need_a = {KIND_TENSOR: 1, KIND_ROW: M, KIND_GROUP128_UE8M0: M * G,
               KIND_GROUP128_FP32: M * G}[kind_a]

@@ -353,6 +353,10 @@ def test_binding_rejects_outputs_and_operands_too_small_before_any_call():
                                                      c=torch.zeros(1, 8, 8, dtype=BF))),
         (ValueError, lambda: fp8sm.scaled_mm_batched(codes[None], w[:, :64], ones(8), ones(16),
                                                      ROW, COL)),
+        (ValueError, lambda: fp8sm.scaled_mm_batched(codes[None], w, ones(8), ones(16), ROW, COL,
+                                                     bias=torch.zeros(8, dtype=BF))),
+        (ValueError, lambda: fp8sm.scaled_mm(codes, w, ones(8), ones(16), ROW, COL,
+                                             bias=torch.zeros(8, dtype=BF))),
         (ValueError, lambda: fp8sm.requantize_max_scale(w, ones(1), [16],
                                                         q=torch.zeros(8, 256, dtype=U8))),
         (ValueError, lambda: fp8sm.requantize_max_scale(w, ones(1), [8, 8])),
