@@ -156,12 +156,15 @@ def quant_group(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul
         group = K_out
     if q is None:
         q = torch.empty((M, K_out), dtype=torch.uint8, device=x.device)
-    _unit_last(q, "q")
-    _holds(q, (M, K_out), "q", torch.uint8)
+    else:
+        _unit_last(q, "q")
+        _holds(q, (M, K_out), "q", torch.uint8)
     if scales is None:
         scales = torch.empty(scale_shape(fmt, layout, M, K_out, group), dtype=_scale_dtype(fmt),
                              device=x.device)
-    _holds_bytes(scales, scale_bytes(fmt, layout, M, K_out, group), "scales", _scale_dtype(fmt))
+    else:
+        _holds_bytes(scales, scale_bytes(fmt, layout, M, K_out, group), "scales",
+                     _scale_dtype(fmt))
     st = _load().fp8sm_quant_group(_ptr(x), _dtype_code(x), M, K_out, _ld(x), group,
                                    FUSE_SILU_MUL if fuse_silu_mul else 0, fmt, layout,
                                    _ptr(q), _ld(q), _ptr(scales), _stream(stream))
@@ -175,8 +178,9 @@ def quant_static(x, scale, q=None, stream=None):
     _unit_last(x, "x")
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    _unit_last(q, "q")
-    _holds(q, (M, K), "q", torch.uint8)
+    else:
+        _unit_last(q, "q")
+        _holds(q, (M, K), "q", torch.uint8)
     _holds_bytes(scale, 4, "scale", torch.float32)
     st = _load().fp8sm_quant_static(_ptr(x), _dtype_code(x), M, K, _ld(x), _ptr(scale),
                                     _ptr(q), _ld(q), _stream(stream))
@@ -189,12 +193,15 @@ def quant_weight_block128(w, q=None, scales=None, stream=None):
     _unit_last(w, "w")
     if q is None:
         q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
-    _unit_last(q, "q")
-    _holds(q, (N, K), "q", torch.uint8)
+    else:
+        _unit_last(q, "q")
+        _holds(q, (N, K), "q", torch.uint8)
     if scales is None:
         scales = torch.empty(((N + 127) // 128, (K + 127) // 128), dtype=torch.float32,
                              device=w.device)
-    _holds_bytes(scales, 4 * ((N + 127) // 128) * ((K + 127) // 128), "scales", torch.float32)
+    else:
+        _holds_bytes(scales, 4 * ((N + 127) // 128) * ((K + 127) // 128), "scales",
+                     torch.float32)
     st = _load().fp8sm_quant_weight_block128(_ptr(w), _dtype_code(w), N, K, _ld(w), _ptr(q),
                                              _ld(q), _ptr(scales), _stream(stream))
     _check(st, "fp8sm_quant_weight_block128")
@@ -208,8 +215,9 @@ def silu_mul_f32(x, y=None, stream=None):
     K = K2 // 2
     if y is None:
         y = torch.empty((M, K), dtype=torch.float32, device=x.device)
-    _unit_last(y, "y")
-    _holds(y, (M, K), "y", torch.float32)
+    else:
+        _unit_last(y, "y")
+        _holds(y, (M, K), "y", torch.float32)
     st = _load().fp8sm_silu_mul_f32(_ptr(x), _dtype_code(x), M, K, _ld(x), _ptr(y),
                                     _ld(y), _stream(stream))
     _check(st, "fp8sm_silu_mul_f32")
@@ -228,12 +236,15 @@ def scaled_mm(a, b, sa, sb, kind_a, kind_b, c=None, M=None, stream=None, bias=No
     _unit_last(b, "b")
     if out_dtype is None:
         out_dtype = c.dtype if c is not None else torch.bfloat16
+    if a.dtype != torch.uint8 or b.dtype != torch.uint8:
+        raise TypeError("a and b must be uint8 E4M3FN codes")
+    if M > Mx or b.dim() != 2 or b.shape[1] < K:
+        raise ValueError(f"a [{Mx}, {K}] / b {tuple(b.shape)} do not hold an M={M}, K={K} product")
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=b.device)
-    _unit_last(c, "c")
-    _holds(a, (M, K), "a", torch.uint8)
-    _holds(b, (N, K), "b", torch.uint8)
-    _holds(c, (M, N), "c")
+    else:
+        _unit_last(c, "c")
+        _holds(c, (M, N), "c")
     _holds_scale(sa, kind_a, M, N, K, "sa")
     _holds_scale(sb, kind_b, M, N, K, "sb")
     if bias is not None:
@@ -291,8 +302,15 @@ def _holds(t, shape, what, dtype=None):
     """The C ABI cannot see buffer sizes: a tensor the caller supplies must
     span at least `shape` (dimension by dimension) and have the dtype the
     call reads or writes, checked here before any call."""
-    if t.dim() != len(shape) or any(have < need for have, need in zip(t.shape, shape)):
-        raise ValueError(f"{what}: needs shape {tuple(shape)}, got {tuple(t.shape)}")
+    sh = t.shape
+    ok = len(sh) == len(shape)
+    if ok:
+        for have, need in zip(sh, shape):
+            if have < need:
+                ok = False
+                break
+    if not ok:
+        raise ValueError(f"{what}: needs shape {tuple(shape)}, got {tuple(sh)}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{what}: needs dtype {dtype}, got {t.dtype}")
 
@@ -313,15 +331,22 @@ def _scale_dtype(fmt):
 def _holds_scale(t, kind, M, N, K, what):
     """A GEMM scale operand holds its kind's elements (bytes for
     GROUP128_UE8M0, fp32 otherwise; unknown kinds are left to the ABI)."""
-    G = (K + 127) // 128
-    elems = {KIND_TENSOR: 1, KIND_ROW: M, KIND_COL: N, KIND_GROUP128_UE8M0: M * G,
-             KIND_GROUP128_FP32: M * G, KIND_BLOCK128: ((N + 127) // 128) * G}.get(kind)
-    if elems is None:
+    if kind == KIND_TENSOR:
+        nbytes = 4
+    elif kind == KIND_ROW:
+        nbytes = 4 * M
+    elif kind == KIND_COL:
+        nbytes = 4 * N
+    elif kind == KIND_GROUP128_FP32:
+        nbytes = 4 * M * ((K + 127) // 128)
+    elif kind == KIND_BLOCK128:
+        nbytes = 4 * ((N + 127) // 128) * ((K + 127) // 128)
+    elif kind == KIND_GROUP128_UE8M0:
+        _holds_bytes(t, M * ((K + 127) // 128), what, torch.uint8)
         return
-    if kind == KIND_GROUP128_UE8M0:
-        _holds_bytes(t, elems, what, torch.uint8)
     else:
-        _holds_bytes(t, 4 * elems, what, torch.float32)
+        return
+    _holds_bytes(t, nbytes, what, torch.float32)
 
 
 def quant_group_batched(x, group, fmt=SCALE_FP32, layout=LAYOUT_ROW_MAJOR, fuse_silu_mul=False,
