@@ -458,7 +458,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        # the arithmetic: fp8 codes widened exactly to bf16, multiplied on the
+        # bf16 matrix cores with fp32 accumulation (the roofline's peak)
+        "dtype": "bf16",
+        "operand_dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: per-token quant bf16[{M},{K}] + rowwise "
                                f"fp8_scaled_mm {M}x{K}x{N} -> bf16",
