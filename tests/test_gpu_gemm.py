@@ -290,6 +290,18 @@ def test_decode_workload_per_tensor(N):
     assert_within_tolerance(outs[16], res, inputs.DECODE_K, f"decode N={N}")
     for M in inputs.DECODE_MS:
         assert np.array_equal(outs[M], outs[16][:M]), M
+    # the weight stored at the padded row stride (K + 64) recommended for
+    # small-M calls, quantized straight into that layout: codes and every
+    # output bitwise equal to the compact layout's, padding bytes untouched
+    K = inputs.DECODE_K
+    wpad = torch.full((N, K + 64), 0x5A, dtype=torch.uint8, device=cuda())
+    qwp = fp8sm.quant_static(d.w[N].to(cuda()), ws, q=wpad[:, :K])
+    for M in inputs.DECODE_MS:
+        c = fp8sm.scaled_mm(qx[:M], qwp, xs, ws, T, T)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(c), outs[M]), f"padded weight M={M}"
+    assert np.array_equal(qwp.cpu().numpy(), ow)
+    assert torch.all(wpad[:, K:] == 0x5A)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
