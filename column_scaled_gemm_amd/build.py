@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp8sm.so")
 
-SOURCES = ["quant.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "probe.hip", "api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

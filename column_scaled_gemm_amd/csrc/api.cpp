@@ -345,7 +345,8 @@ static fp8sm_status scaled_mm_impl(const uint8_t* A, int64_t lda, const uint8_t*
                                    fp8sm_scale_kind ka, const void* sa, fp8sm_scale_kind kb,
                                    const void* sb, const void* bias, fp8sm_dtype out,
                                    hipStream_t stream,
-                                   const GemmBatch& bt = GemmBatch{1, 0, 0, 0, 0, 0, nullptr}) {
+                                   const GemmBatch& bt = GemmBatch{1, 0, 0, 0, 0, 0, nullptr},
+                                   bool fp8mfma = false) {
   fp8sm_status bst = check_batch(bt.count, bt.rows, {bt.a, bt.b, bt.c, bt.sa, bt.sb});
   if (bst != FP8SM_OK) return bst;
   const bool rowwise = (ka == FP8SM_KIND_TENSOR || ka == FP8SM_KIND_ROW) &&
@@ -393,6 +394,7 @@ static fp8sm_status scaled_mm_impl(const uint8_t* A, int64_t lda, const uint8_t*
   g.bias = bias;
   g.out_f16 = out == FP8SM_FP16;
   g.batch = bt;
+  if (fp8mfma) return launched(launch_gemm_rowwise_fp8mfma(g, stream));
   if (blockwise) return launched(launch_gemm_blockwise(g, stream));
   int v = fp8sm_pick_variant(M, N, K);
   if (!variant_accepts(v, M)) return FP8SM_ERR_UNSUPPORTED;
@@ -413,6 +415,27 @@ fp8sm_status fp8sm_scaled_mm_ex(const uint8_t* A, int64_t lda, const uint8_t* B,
                                 const void* sb, const void* bias, fp8sm_dtype out,
                                 hipStream_t stream) {
   return scaled_mm_impl(A, lda, B, ldb, C, ldc, M, N, K, ka, sa, kb, sb, bias, out, stream);
+}
+
+fp8sm_status fp8sm_scaled_mm_fp8mfma(const uint8_t* A, int64_t lda, const uint8_t* B,
+                                     int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N,
+                                     int64_t K, fp8sm_scale_kind ka, const void* sa,
+                                     fp8sm_scale_kind kb, const void* sb, hipStream_t stream) {
+  const bool rowwise = (ka == FP8SM_KIND_TENSOR || ka == FP8SM_KIND_ROW) &&
+                       (kb == FP8SM_KIND_TENSOR || kb == FP8SM_KIND_COL);
+  if (!rowwise) return FP8SM_ERR_UNSUPPORTED;
+  return scaled_mm_impl(A, lda, B, ldb, C, ldc, M, N, K, ka, sa, kb, sb, nullptr, FP8SM_BF16,
+                        stream, GemmBatch{1, 0, 0, 0, 0, 0, nullptr}, true);
+}
+
+fp8sm_status fp8sm_mfma_probe(int32_t instr, const uint32_t* a_regs, const uint32_t* b_regs,
+                              float* d_regs, hipStream_t stream) {
+  if (instr < 0 || instr > 4) return FP8SM_ERR_UNSUPPORTED;
+  if (!a_regs || !b_regs || !d_regs) return FP8SM_ERR_NULL;
+  if (!aligned(a_regs, 16) || !aligned(b_regs, 16) || !aligned(d_regs, 16)) return FP8SM_ERR_ALIGN;
+  fp8sm_status st = check_device();
+  if (st != FP8SM_OK) return st;
+  return launched(launch_mfma_probe(instr, a_regs, b_regs, d_regs, stream));
 }
 
 fp8sm_status fp8sm_scaled_mm_batched(int64_t nbatch, const int32_t* rows, const uint8_t* A,

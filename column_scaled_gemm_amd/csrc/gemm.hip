@@ -446,10 +446,120 @@ __global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
   }
 }
 
-// fp64 -> bf16 with one rounding (nearest even) for results in the bf16
-// normal range; smaller magnitudes, zeros and NaN go through fp32.
+// ---------------------------------------------------------------------------
+// The rowwise GEMM on the fp8 matrix instructions (v_mfma_f32_32x32x64_f8f6f4,
+// e4m3 x e4m3): no widening, twice the matrix rate of the bf16 path.  It is
+// kept only as measured evidence for the choice of the bf16 path: these
+// instructions sum each run of products with the smaller ones truncated far
+// below fp32 precision, so the result misses the accuracy bound on outputs
+// that nearly cancel.  The shape dispatch never selects it; it is reached
+// only through its own test entry point.  Same DMA ring and tile walk as
+// gemm_rowwise_kernel; wavefronts of BM/2 x BN/2 in 32 x 32 subtiles; lane
+// half h holds k = 32h .. 32h + 31 of each 64-wide chunk for both operands
+// (the same register positions carry the same k in A and B, so the products
+// pair up whatever order the instruction sums them in).
+template <int BM, int BN, int NSLOT, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_rowwise_fp8mfma_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
+    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
+    int sa_vec, const float* __restrict__ sb, int sb_vec, int tiles_m, int tiles_n) {
+  constexpr int TM = BM / 64, TN = BN / 64;  // 32-row subtiles per wavefront
+  constexpr int ROWS = BM + BN;
+  constexpr int SLOT = ROWS * kChunk;
+  constexpr int SEGS = SLOT / 1024;
+  constexpr int DPS = SEGS / 4;
+  static_assert(NSLOT >= 2 && NSLOT <= 4, "ring depth");
+  static_assert(SEGS % 4 == 0, "segments must split over the four wavefronts");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSLOT * SLOT];
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
+
+  DmaPlan<DPS, BM> dma;
+  dma.init(A, lda, B, ldb, m0, n0, M, N, w, lane);
+  const int nkc = (K + kChunk - 1) / kChunk;
+  auto issue = [&](int kc) {
+    dma.issue(lds0 + (uint32_t)((kc % NSLOT) * SLOT), kc * kChunk, K, w);
+  };
+  const int a_off0 = wm * (BM / 2) * kChunk + frag32_off(lane, 0);
+  const int a_off1 = wm * (BM / 2) * kChunk + frag32_off(lane, 1);
+  const int b_off0 = (BM + wn * (BN / 2)) * kChunk + frag32_off(lane, 0);
+  const int b_off1 = (BM + wn * (BN / 2)) * kChunk + frag32_off(lane, 1);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  for (int c = 0; c < NSLOT - 1 && c < nkc; ++c) issue(c);
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int after = min(NSLOT - 2, nkc - 1 - kc);
+    if (after >= 2)
+      wait_vmcnt<2 * DPS>();
+    else if (after == 1)
+      wait_vmcnt<DPS>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (kc + NSLOT - 1 < nkc) issue(kc + NSLOT - 1);
+    const uint8_t* slot = lds + (kc % NSLOT) * SLOT;
+    i32x8 fa[TM], fb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint4 p = *reinterpret_cast<const uint4*>(slot + a_off0 + i * 32 * kChunk);
+      const uint4 q = *reinterpret_cast<const uint4*>(slot + a_off1 + i * 32 * kChunk);
+      fa[i] = i32x8{(int)p.x, (int)p.y, (int)p.z, (int)p.w, (int)q.x, (int)q.y, (int)q.z, (int)q.w};
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const uint4 p = *reinterpret_cast<const uint4*>(slot + b_off0 + j * 32 * kChunk);
+      const uint4 q = *reinterpret_cast<const uint4*>(slot + b_off1 + j * 32 * kChunk);
+      fb[j] = i32x8{(int)p.x, (int)p.y, (int)p.z, (int)p.w, (int)q.x, (int)q.y, (int)q.z, (int)q.w};
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0,
+                                                                    0, 0, 0);
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = m0 + wm * (BM / 2) + 32 * i + (lane & 31);
+    if (r >= M) continue;
+    const float sar = sa[sa_vec ? r : 0];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = n0 + wn * (BN / 2) + 32 * j + 8 * v + 4 * (lane >> 5);
+        if (c >= N) continue;
+        const f32x4 a4 = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2],
+                          acc[i][j][4 * v + 3]};
+        store_row4<0>(C, ldc, r, c, a4, sar, sb, sb_vec, nullptr);
+      }
+  }
+}
+
+// fp64 -> bf16 with one rounding (nearest even).  Normal results: rounded to
+// 8 significant bits in fp64, then converted exactly.  Below 2^-126 (the bf16
+// subnormal range, spacing 2^-133): rounded to a multiple of 2^-133 in fp64,
+// which fp32 and then bf16 hold exactly.  Zeros and NaN go through fp32.
 __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
-  if (!(fabs(x) >= 0x1p-126)) return f32_to_bf16_rne((float)x);
+  if (!(fabs(x) >= 0x1p-126)) {
+    const double r = __builtin_rint(x * 0x1p133) * 0x1p-133;  // nearest even multiple
+    return f32_to_bf16_rne((float)r);                         // both conversions exact
+  }
   uint64_t u = (uint64_t)__double_as_longlong(x);
   u += ((uint64_t)1 << 44) - 1 + ((u >> 45) & 1);  // round to 8 significant bits
   u &= ~(((uint64_t)1 << 45) - 1);
@@ -460,11 +570,18 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
 // Blockwise kernel for 1x128 UE8M0 activation groups and 128x128 fp32 weight
 // blocks.  Same ring, chunk order and B-first layout as the rowwise kernel,
 // with a 128 x 128 tile (wavefronts of 64 x 64).  The activation scale
-// 2^(byte - 127) is applied exactly in the widen, so each 128-wide K block's
-// fresh fp32 partial already carries it; the partial is then multiplied by the
-// block's weight scale (one value per tile: the tile spans one 128-column
-// weight block) and added to an fp64 master.  The tile's scale bytes are
-// staged in LDS, SEGB K blocks at a time.
+// 2^(byte - 127) is applied exactly: its exponent clamped to +-kWidenExp in
+// the widen, so each 128-wide K block's fresh fp32 partial already carries
+// it, and the rest (bytes below 27 or above 227) with the block's weight
+// scale (one value per tile: the tile spans one 128-column weight block) in
+// the fp64 factor that adds the partial to an fp64 master.  The tile's scale
+// bytes are staged in LDS, SEGB K blocks at a time.
+//
+// kWidenExp: every finite E4M3 value times 2^e, |e| <= 100, is a bf16 normal,
+// every product of two such operands (the weight unscaled) is an fp32 normal,
+// and a 128-wide block sum stays below 2^125.
+constexpr int kWidenExp = 100;
+
 template <int NSLOT, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
@@ -541,7 +658,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
         mast[i][j][v] = 0.0;
       }
   float asc[TM];
-  double sbk = 0.0;
+  double sbk[TM] = {};  // per row subtile: weight scale x out-of-window power of two
 
   for (int c = 0; c < NSLOT - 1 && c < nkc; ++c) issue(c);
   stage_scales(0);  // visible after the first loop barrier
@@ -564,10 +681,17 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
         stage_scales(kb);
         __syncthreads();
       }
+      // 2^(byte - 127) for any byte: the part of the exponent inside
+      // [-100, 100] goes into the widen (exact there), the rest into the
+      // fp64 factor of the promotion.
+      const double sb64 = (double)sbrow[kb];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        asc[i] = __uint_as_float((uint32_t)escb[(wm * 64 + 32 * i + (lane & 31)) * SEGB + kb % SEGB] << 23);
-      sbk = (double)sbrow[kb];
+      for (int i = 0; i < TM; ++i) {
+        const int e = (int)escb[(wm * 64 + 32 * i + (lane & 31)) * SEGB + kb % SEGB] - 127;
+        const int ein = min(max(e, -kWidenExp), kWidenExp);
+        asc[i] = __uint_as_float((uint32_t)(ein + 127) << 23);
+        sbk[i] = __builtin_ldexp(sb64, e - ein);
+      }
     }
     if (kc + NSLOT - 1 < nkc) issue(kc + NSLOT - 1);
     const uint8_t* slot = lds + (kc % NSLOT) * SLOT;
@@ -594,7 +718,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mast[i][j][v] = fma((double)acc[i][j][v], sbk, mast[i][j][v]);
+        for (int v = 0; v < 16; ++v) mast[i][j][v] = fma((double)acc[i][j][v], sbk[i], mast[i][j][v]);
   }
 
 #pragma unroll
@@ -946,6 +1070,16 @@ hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
     case VAR_DECODE_64: return launch_decode<4, 8>(g, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_rowwise_fp8mfma(const GemmArgs& g, hipStream_t s) {
+  constexpr int BM = 128, BN = 256;
+  const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_rowwise_fp8mfma_kernel<BM, BN, 3, 2>), dim3(tiles_m * tiles_n),
+                     dim3(256), 0, s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N,
+                     (int)g.K, static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
+                     static_cast<const float*>(g.sb), (int)(g.sb_kind == 2), tiles_m, tiles_n);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_blockwise(const GemmArgs& g, hipStream_t s) {

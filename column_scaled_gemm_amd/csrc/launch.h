@@ -113,6 +113,11 @@ const char* variant_name(int v);
 bool variant_accepts(int v, int64_t M);
 hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_blockwise(const GemmArgs& g, hipStream_t s);
+// The rowwise GEMM on the fp8 matrix instructions (evidence only: inexact).
+hipError_t launch_gemm_rowwise_fp8mfma(const GemmArgs& g, hipStream_t s);
+// One matrix instruction on host-supplied register images (probe.hip).
+hipError_t launch_mfma_probe(int instr, const uint32_t* a, const uint32_t* b, float* d,
+                             hipStream_t s);
 hipError_t launch_fill_k0(uint16_t* C, int64_t ldc, int64_t M, int64_t N, const void* bias,
                           hipStream_t s, const GemmBatch& bt = GemmBatch{1, 0, 0, 0, 0, 0, nullptr});
 

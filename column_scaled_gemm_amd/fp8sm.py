@@ -54,9 +54,16 @@ SIGNATURES = {
     "fp8sm_variant_name": (ctypes.c_char_p, [_int]),
     "fp8sm_pick_variant": (_int, [_i64, _i64, _i64]),
     "fp8sm_variant_accepts": (_int, [_int, _i64, _i64, _i64]),
+    "fp8sm_scaled_mm_fp8mfma": (_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _int, _p,
+                                       _int, _p, _p]),
+    "fp8sm_mfma_probe": (_int, [_i32, _p, _p, _p, _p]),
 }
 
 _lib = None
+
+
+class DeviceTensorError(ValueError):
+    """A tensor argument is not on the current GPU (raised before any call)."""
 
 
 class Fp8smError(RuntimeError):
@@ -96,7 +103,19 @@ def _stream(stream=None):
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    """Device address of a tensor argument (NULL for None).  The kernels
+    dereference every such address on the GPU, so a host tensor, or one on
+    another device than the current one, is refused here, before the library
+    is called."""
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not t.is_cuda:
+        raise DeviceTensorError("tensor arguments must be device (cuda) tensors; got one on "
+                                f"{t.device}")
+    if t.device.index != torch.cuda.current_device():
+        raise DeviceTensorError(f"tensor on {t.device}, but the current device is "
+                                f"cuda:{torch.cuda.current_device()}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _dtype_code(t):
@@ -263,6 +282,48 @@ def scaled_mm(a, b, sa, sb, kind_a, kind_b, c=None, M=None, stream=None, bias=No
                                     None if bias is None else _ptr(bias), out, _stream(stream))
     _check(st, "fp8sm_scaled_mm_ex")
     return c
+
+
+def scaled_mm_fp8mfma(a, b, sa, sb, kind_a, kind_b, c=None, stream=None):
+    """Test hook fp8sm_scaled_mm_fp8mfma: the rowwise GEMM on the fp8 matrix
+    instructions (inexact; evidence for the bf16 path, never dispatched)."""
+    M, K = a.shape
+    N = b.shape[0]
+    _unit_last(a, "a")
+    _unit_last(b, "b")
+    if a.dtype != torch.uint8 or b.dtype != torch.uint8:
+        raise TypeError("a and b must be uint8 E4M3FN codes")
+    if b.dim() != 2 or b.shape[1] < K:
+        raise ValueError(f"b {tuple(b.shape)} does not hold an N x {K} operand")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=b.device)
+    else:
+        _unit_last(c, "c")
+        _holds(c, (M, N), "c", torch.bfloat16)
+    _holds_scale(sa, kind_a, M, N, K, "sa")
+    _holds_scale(sb, kind_b, M, N, K, "sb")
+    st = _load().fp8sm_scaled_mm_fp8mfma(_ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(c), _ld(c),
+                                         M, N, K, kind_a, _ptr(sa), kind_b, _ptr(sb),
+                                         _stream(stream))
+    _check(st, "fp8sm_scaled_mm_fp8mfma")
+    return c
+
+
+MFMA_BF16_16x16x32, MFMA_BF16_32x32x16 = 0, 1
+MFMA_F8_16x16x128, MFMA_F8_32x32x64, MFMA_F8_16x16x32 = 2, 3, 4
+
+
+def mfma_probe(instr, a_regs, b_regs, stream=None):
+    """Test hook fp8sm_mfma_probe: a_regs, b_regs device uint32-compatible
+    [64, 8] register images (int32 tensors) -> device float32 [64, 16] result
+    registers of one matrix instruction with a zero accumulator."""
+    for t, what in ((a_regs, "a_regs"), (b_regs, "b_regs")):
+        if t.dtype != torch.int32 or tuple(t.shape) != (64, 8) or not t.is_contiguous():
+            raise ValueError(f"{what} must be a contiguous int32 [64, 8] tensor")
+    d = torch.zeros((64, 16), dtype=torch.float32, device=a_regs.device)
+    st = _load().fp8sm_mfma_probe(instr, _ptr(a_regs), _ptr(b_regs), _ptr(d), _stream(stream))
+    _check(st, "fp8sm_mfma_probe")
+    return d
 
 
 # ---------------------------------------------------------------- batched calls

@@ -336,6 +336,42 @@ int fp8sm_pick_variant(int64_t M, int64_t N, int64_t K);
  * the call accepts. */
 int fp8sm_variant_accepts(int id, int64_t M, int64_t N, int64_t K);
 
+/*
+ * Test hook (evidence, not part of the path): the rowwise / per-tensor GEMM
+ * of fp8sm_scaled_mm computed on the fp8 matrix instructions
+ * (v_mfma_f32_32x32x64_f8f6f4, e4m3 x e4m3) instead of the bf16 ones.  These
+ * instructions sum each run of products with the smaller ones truncated well
+ * below fp32 precision (fp8sm_mfma_probe measures it), so outputs that nearly
+ * cancel miss the accuracy bound of the pages' GEMM ([P1] Summary: fp32
+ * accumulation of E4M3FN products); the shape dispatch never uses it, and
+ * its rows need not equal fp8sm_scaled_mm's.  Arguments, rules and errors are
+ * those of fp8sm_scaled_mm; blockwise kinds -> ERR_UNSUPPORTED.
+ */
+fp8sm_status fp8sm_scaled_mm_fp8mfma(const uint8_t* A, int64_t lda, const uint8_t* B,
+                                     int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N,
+                                     int64_t K, fp8sm_scale_kind ka, const void* sa,
+                                     fp8sm_scale_kind kb, const void* sb, hipStream_t stream);
+
+/*
+ * Test hook: one wavefront executes one matrix instruction with a zero
+ * accumulator on register images given by the caller, and writes the result
+ * registers back -- the probe of how each instruction sums its products (the
+ * reason the GEMMs widen fp8 to bf16 before the matrix cores, [P1] Summary:
+ * fp32 accumulation).
+ *   instr  0: v_mfma_f32_16x16x32_bf16      (a, b: 4 dwords/lane; d: 4 floats)
+ *          1: v_mfma_f32_32x32x16_bf16      (a, b: 4 dwords/lane; d: 16 floats)
+ *          2: v_mfma_f32_16x16x128_f8f6f4   (e4m3 x e4m3; 8 dwords; d: 4 floats)
+ *          3: v_mfma_f32_32x32x64_f8f6f4    (e4m3 x e4m3; 8 dwords; d: 16 floats)
+ *          4: v_mfma_f32_16x16x32_fp8_fp8   (2 dwords; d: 4 floats)
+ *   a_regs, b_regs  device uint32 [64][8]: lane-major register images of the
+ *          instruction's first and second operands (unused dwords ignored).
+ *   d_regs device float [64][16]: lane-major result registers (unused ones 0).
+ * All three 16-byte aligned.  Errors: instr out of range -> ERR_UNSUPPORTED;
+ * NULL -> ERR_NULL; alignment -> ERR_ALIGN.
+ */
+fp8sm_status fp8sm_mfma_probe(int32_t instr, const uint32_t* a_regs, const uint32_t* b_regs,
+                              float* d_regs, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

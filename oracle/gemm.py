@@ -130,10 +130,22 @@ def scaled_mm(a_codes, b_codes, sa, sb, bias=None, out="bf16"):
     return MMResult(to_bf16_bits(value), value, acc, sab)
 
 
+def ue8m0_values(e_bytes):
+    """Scale values of UE8M0 exponent bytes: 2^(byte - 127), exact, as float64
+    (the storage form 2^(e-127) of sglang PR #33533, Modifications 3).  Every
+    byte 0..255 is taken as a power of two; bytes 0 and 255 give 2^-127 and
+    2^128, outside the fp32 normal range (the latter beyond fp32 itself)."""
+    e = np.asarray(e_bytes)
+    if e.dtype != np.uint8:
+        raise ValueError("UE8M0 scales are bytes")
+    return np.ldexp(np.ones(e.shape), e.astype(np.int64) - 127)
+
+
 def blockwise_mm(a_codes, a_scale, b_codes, b_scale, block=128):
     """Blockwise scaled GEMM.
 
-    a_scale: [M, ceil(K/block)] scale values (for UE8M0, 2^e as float32);
+    a_scale: [M, ceil(K/block)] scale values: float32 values, or float64 as
+    given (ue8m0_values for UE8M0 bytes, which may lie beyond fp32);
     b_scale: [ceil(N/block), ceil(K/block)] float32.
     Returns (MMResult with sab = max_kb a_scale * b_scale, the per-output
     scale magnitude the tolerance uses).
@@ -143,7 +155,10 @@ def blockwise_mm(a_codes, a_scale, b_codes, b_scale, block=128):
     M, K = a_codes.shape
     N = b_codes.shape[0]
     KB = -(-K // block)
-    a_scale = np.asarray(a_scale, dtype=np.float32).reshape(M, KB).astype(np.float64)
+    a_scale = np.asarray(a_scale)
+    if a_scale.dtype != np.float64:
+        a_scale = a_scale.astype(np.float32)
+    a_scale = a_scale.reshape(M, KB).astype(np.float64)
     b_scale = np.asarray(b_scale, dtype=np.float32).reshape(-(-N // block), KB).astype(np.float64)
     nb_of_n = np.arange(N) // block
     total = np.zeros((M, N), dtype=np.float64)

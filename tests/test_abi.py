@@ -365,5 +365,41 @@ def test_binding_rejects_outputs_and_operands_too_small_before_any_call():
                                                        q=torch.zeros(8, 256, dtype=U8))),
     ]
     for i, (err, call) in enumerate(cases):
-        with pytest.raises(err):
+        with pytest.raises(err) as info:
+            call()
+        # the size / dtype check itself fired, not the later device check
+        assert not isinstance(info.value, fp8sm.DeviceTensorError), i
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    # the kernels dereference every tensor address on the GPU: host tensors of
+    # valid shapes are refused by the binding before the library is called
+    import torch
+    from column_scaled_gemm_amd import fp8sm
+    ROW, COL, U8, BF = fp8sm.KIND_ROW, fp8sm.KIND_COL, torch.uint8, torch.bfloat16
+    x = torch.zeros(8, 256, dtype=BF)
+    codes = torch.zeros(8, 256, dtype=U8)
+    w = torch.zeros(16, 256, dtype=U8)
+    ones = torch.ones
+    calls = [
+        lambda: fp8sm.quant_group(x, 128),
+        lambda: fp8sm.quant_group(x, -1, fuse_silu_mul=True),
+        lambda: fp8sm.quant_static(x, ones(1)),
+        lambda: fp8sm.quant_weight_block128(x),
+        lambda: fp8sm.silu_mul_f32(x),
+        lambda: fp8sm.scaled_mm(codes, w, ones(8), ones(16), ROW, COL),
+        lambda: fp8sm.scaled_mm(codes, w, ones(8), ones(16), ROW, COL,
+                                bias=torch.zeros(16, dtype=BF)),
+        lambda: fp8sm.scaled_mm_fp8mfma(codes, w, ones(8), ones(16), ROW, COL),
+        lambda: fp8sm.quant_group_batched(x[None], 128),
+        lambda: fp8sm.quant_static_batched(x[None], ones(1)),
+        lambda: fp8sm.scaled_mm_batched(codes[None], w, ones(8), ones(16), ROW, COL),
+        lambda: fp8sm.requantize_max_scale(w, ones(1), [16]),
+        lambda: fp8sm.scales_to_channelwise(ones(2), [8, 8]),
+        lambda: fp8sm.quant_group_scatter(x, torch.zeros(8, 2, dtype=torch.int32), 16),
+        lambda: fp8sm.mfma_probe(0, torch.zeros(64, 8, dtype=torch.int32),
+                                 torch.zeros(64, 8, dtype=torch.int32)),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(fp8sm.DeviceTensorError):
             call()

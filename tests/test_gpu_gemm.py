@@ -498,3 +498,34 @@ def test_quant_and_rowwise_gemm_graph_replays(M, variant):
             assert_within_tolerance(cg, res, K, f"graph replay M={M} {variant}")
     finally:
         fp8sm.force_variant(prev)
+
+
+def test_blockwise_ue8m0_every_exponent_byte():
+    # UE8M0 scales are 2^(byte - 127) for every byte 0..255.  Row r has one
+    # live K block, with byte r, whose weight scale 2^s brings byte r's
+    # power of two back near 1 (so every output is a normal, finite bf16);
+    # its other blocks hold zero codes with random bytes (extremes
+    # included).  Checked against the oracle with the bound's sa * sb taken
+    # from the live block alone (stricter than the max over blocks).
+    M, N, G = 256, 256, 5
+    K = 128 * G
+    print("[case] blockwise ue8m0 every byte M=256 N=256 K=640", flush=True)
+    offs = np.array([110, 50, 0, -50, -110])
+    r = inputs.rng(255)
+    live = np.array([int(np.argmin(np.abs(b - 127 + offs))) for b in range(M)])
+    A = np.zeros((M, K), np.uint8)
+    codes = e4m3.finite_codes()
+    for m in range(M):
+        kb = live[m]
+        A[m, 128 * kb:128 * (kb + 1)] = codes[r.integers(0, codes.size, 128)]
+    B = codes[r.integers(0, codes.size, (N, K))]
+    e = r.integers(0, 256, (M, G)).astype(np.uint8)
+    e[np.arange(M), live] = np.arange(M)
+    sb = np.tile(np.exp2(offs.astype(np.float64)).astype(F32), ((N + 127) // 128, 1))
+    c = fp8sm.scaled_mm(to_gpu_u8(A), to_gpu_u8(B), torch.from_numpy(e).to(cuda()),
+                        to_gpu_f32(sb), fp8sm.KIND_GROUP128_UE8M0, fp8sm.KIND_BLOCK128)
+    torch.cuda.synchronize()
+    res = og.blockwise_mm(A, og.ue8m0_values(e), B, sb)
+    res.sab = (og.ue8m0_values(e)[np.arange(M), live] * np.exp2(offs[live]))[:, None] * np.ones((1, N))
+    assert np.all(np.isfinite(res.out)) and np.all(np.abs(res.out[res.out != 0]) >= 2.0 ** -126)
+    assert_within_tolerance(bf16_bits(c), res, K, "ue8m0 every byte")

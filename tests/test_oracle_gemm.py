@@ -262,3 +262,44 @@ def test_zero_bias_is_no_bias_and_matches_torch_casts():
         r = gemm.scaled_mm(A, B, sa, sb, bias=bias, out=out)
         ref = v.to(tdt).view(torch.int16).numpy().view(np.uint16).astype(np.int32)
         assert np.max(np.abs(r.bits.astype(np.int32) - ref)) <= 1
+
+
+def test_ue8m0_values_follow_the_ieee_biased_exponent():
+    # byte b in 1..254 is the biased exponent field of an fp32 power of two:
+    # the float32 whose bit pattern is b << 23; byte 0 is 2^-127 (the fp32
+    # subnormal with only bit 22 set), byte 255 is twice fp32's 2^127
+    b = np.arange(256, dtype=np.uint8)
+    v = gemm.ue8m0_values(b)
+    assert v.dtype == np.float64
+    ieee = (b[1:255].astype(np.uint32) << 23).view(np.float32).astype(np.float64)
+    assert np.array_equal(v[1:255], ieee)
+    assert v[0] == np.array([0x00400000], np.uint32).view(np.float32).astype(np.float64)[0]
+    assert v[255] == 2.0 * np.array([254 << 23], np.uint32).view(np.float32).astype(np.float64)[0]
+    assert v[127] == 1.0
+
+
+def test_blockwise_extreme_ue8m0_scales_closed_forms():
+    # one-hot products 1 x 1 in each of three K blocks with scales 2^128
+    # (byte 255), 2^-127 (byte 0) and 1: out = sb * (2^128 + 2^-127 + 1) in
+    # float64, rounded once to bf16; with sb = 2^-10, bf16(2^118 + ...) is
+    # 2^118 (bits 245 << 7); a row with only the byte-0 block gives 2^-137,
+    # below half the smallest bf16 subnormal 2^-133 (+0), and with sb = 1
+    # 2^-127 = the subnormal 64 x 2^-133 (bits 0x0040); a row whose byte-255
+    # block is the only live one overflows to +inf with sb = 1
+    K = 384
+    A = np.zeros((3, K), np.uint8)
+    B = np.zeros((8, K), np.uint8)
+    one = e4m3.encode(np.array([1.0], F32))[0]
+    for kb in range(3):
+        A[0, 128 * kb + 5] = one
+        B[:, 128 * kb + 5] = one
+    A[1, 128 * 1 + 5] = one
+    A[2, 5] = one
+    e = np.array([[255, 0, 127], [255, 0, 127], [255, 0, 127]], np.uint8)
+    r = gemm.blockwise_mm(A, gemm.ue8m0_values(e), B, np.full((1, 3), 2.0 ** -10, F32))
+    assert np.all(r.bits[0] == 245 << 7)
+    assert np.all(r.bits[1] == 0)
+    assert np.all(r.bits[2] == 245 << 7)
+    r = gemm.blockwise_mm(A, gemm.ue8m0_values(e), B, np.ones((1, 3), F32))
+    assert np.all(r.bits[1] == 0x0040)
+    assert np.all(r.bits[2] == 0x7F80)                     # 2^128 > bf16 max: +inf
