@@ -10,16 +10,26 @@
 // dispatch picked (the property sglang PR #44861's reviewers checked row by
 // row):
 //  * fp8 codes are widened exactly to bf16 in registers and multiplied on the
-//    bf16 matrix cores (v_mfma_f32_16x16x32_bf16).  The fp8 matrix
-//    instructions were measured to sum each run of 8 products with the
-//    smaller ones truncated ~13 bits below the largest -- far outside fp32
-//    accumulation; the bf16 instruction keeps near-fp32 precision.
-//  * K is walked in 64-wide chunks, ascending.  Within a chunk, MFMA step s
-//    (0, 1) of lane group g (0..3) multiplies k = 16g + 8s + j, j = 0..7.
-//    Positions past K hold zero codes.
-//  * One fp32 accumulator per output is chained through every step, starting
-//    from zero (fp32 accumulation, as the path is specified).
-//  * Epilogue: bf16_rne((acc * sa[m]) * sb[n]).
+//    bf16 matrix cores (v_mfma_f32_32x32x16_bf16).  The fp8 matrix
+//    instructions sum each run of 8 products with the smaller ones truncated
+//    ~13 bits below the largest (measured through fp8sm_mfma_probe), far
+//    outside fp32 accumulation; the bf16 instruction keeps fp32 precision.
+//  * K is walked in 64-wide chunks, ascending; positions past K hold zero
+//    codes.  Within a chunk, matrix step s (0..3) multiplies the 16 positions
+//    k = 32h + 8s + j, h = 0, 1, j = 0..7 (lane half h of the instruction
+//    holds k = 32h .. 32h + 31 of its row), one instruction per 32 x 32
+//    output subtile: the step adds the 16 products to its accumulator operand
+//    and rounds once to fp32.
+//  * The chunks are grouped in blocks of kBlockChunks (512 K).  A block's
+//    fp32 partial starts at +0 and is chained through the block's 32 steps;
+//    it is then added (fp32, round to nearest) into the output's fp32 master,
+//    which starts at +0; blocks ascending.  (One fp32 chain over all of K lets
+//    the accumulator reach ~3e5 code-product units on the H3 workloads, whose
+//    rounding left one gate/up output beyond the accuracy bound; per-block
+//    partials keep the chain's magnitude, and so its rounding, several times
+//    smaller.  Blocks are also what lets the decode kernel run several
+//    chains at once without changing any result.)
+//  * Epilogue: bf16_rne((master * sa[m]) * sb[n]).
 //
 // Blockwise (1x128 activation groups x 128x128 weight blocks): a fresh fp32
 // partial per 128-wide K block, multiplied by sa[m,kb] * sb[n/128,kb] in fp64
@@ -37,7 +47,8 @@
 
 namespace fp8sm {
 
-constexpr int kChunk = 64;  // K bytes per pipeline stage / canonical chunk
+constexpr int kChunk = 64;        // K bytes per pipeline stage / canonical chunk
+constexpr int kBlockChunks = 8;   // chunks per fp32 partial of the rowwise path (512 K)
 
 __device__ __forceinline__ bf16x8 widen_e4m3_x8(uint32_t d0, uint32_t d1) {
   const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
@@ -53,31 +64,6 @@ __device__ __forceinline__ bf16x8 widen_e4m3_x8_scaled(uint32_t d0, uint32_t d1,
   const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false);
   const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true);
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// One canonical 64-wide chunk for TM x TN 16x16 output tiles: fa/fb hold each
-// lane's 16 bytes (k = 16g .. 16g+15 of the chunk) per row / column subtile.
-// Rowwise form: B is the instruction's first operand, so acc[i][j] holds the
-// transposed tile -- lane l has row 16i + l%16 and the four consecutive
-// columns 16j + 4(l/16) .. +3, which the epilogue stores as one 8-byte write.
-template <int TM, int TN>
-__device__ __forceinline__ void mma_chunk64_bt(const uint4 (&fa)[TM], const uint4 (&fb)[TN],
-                                               f32x4 (&acc)[TM][TN]) {
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    bf16x8 a[TM], b[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-      a[i] = s == 0 ? widen_e4m3_x8(fa[i].x, fa[i].y) : widen_e4m3_x8(fa[i].z, fa[i].w);
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      b[j] = s == 0 ? widen_e4m3_x8(fb[j].x, fb[j].y) : widen_e4m3_x8(fb[j].z, fb[j].w);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-  }
 }
 
 // Same chunk with A as the first operand (blockwise kernel: lane l has column
@@ -139,6 +125,17 @@ __device__ __forceinline__ void mma32_step(const Frag32 (&fa)[TM], const float (
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], FRESH ? zero : acc[i][j], 0, 0, 0);
+}
+
+// master += partial, elementwise in fp32 (the end of a canonical block).
+template <int TM, int TN>
+__device__ __forceinline__ void promote_block(const f32x16 (&acc)[TM][TN], f32x16 (&mast)[TM][TN]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mast[i][j][v] = mast[i][j][v] + acc[i][j][v];
 }
 
 // With SCALED, A row subtile i is widened times asc[i], a power of two: the
@@ -300,38 +297,36 @@ __device__ __forceinline__ void dma16_buf(uint32_t voff, i32x4 rsrc, int soff, u
 #pragma clang diagnostic pop
 
 // Copy plan of one wavefront for a ring stage of the BM + BN row tile (A rows
-// then B rows): copy i of wavefront w fills 16-row segment 4i + w; lane l
-// copies row 16 seg + l/4, 16-byte piece (l%4) ^ swz16(l/4) of the 64-byte
-// chunk, so the slot holds swizzled rows.  Rows past M / N repeat the last
+// then B rows): copy i of wavefront w (of NW) fills 16-row segment NW i + w;
+// lane l copies row 16 seg + l/4, 16-byte piece (l%4) ^ swz16(l/4) of the
+// 64-byte chunk, so the slot holds swizzled rows.  Rows past M / N repeat the last
 // row.  Whole chunks are copied by buffer loads from a per-segment SGPR
 // descriptor with the chunk offset in a scalar register (no vector
 // instruction per copy; row strides <= 2^24 keep 15 rows + K below 2^31);
 // a partial last chunk (K % 64 != 0) takes guarded global copies that read
 // zeros past K.
-template <int DPS, int BM>
+template <int DPS, int BM, int NW = 4>
 struct DmaPlan {
-  const uint8_t* src[DPS];
-  int koff[DPS];
-  i32x4 rs[DPS];
-  uint32_t vo[DPS];
+  i32x4 rs[DPS];     // per-segment descriptor (wave-uniform: SGPRs)
+  uint32_t vo[DPS];  // the lane's byte offset from its segment's base
+  int koff;          // the lane's 16-byte piece within a chunk row (every segment)
 
   __device__ __forceinline__ void init(const uint8_t* A, int64_t lda, const uint8_t* B,
                                        int64_t ldb, int m0, int n0, int M, int N, int w,
                                        int lane) {
+    const int r = lane >> 2;
+    koff = ((lane & 3) ^ swz16(r)) * 16;
 #pragma unroll
     for (int i = 0; i < DPS; ++i) {
-      const int seg = i * 4 + w;
-      const int r = lane >> 2;
-      koff[i] = ((lane & 3) ^ swz16(r)) * 16;
+      const int seg = i * NW + w;
       const bool isa = seg * 16 < BM;
       const uint8_t* base = isa ? A : B;
       const int64_t ld = isa ? lda : ldb;
       const int first = isa ? m0 + seg * 16 : n0 + seg * 16 - BM;
       const int last = (isa ? M : N) - 1;
       const int r0 = min(first, last), rr = min(first + r, last);
-      src[i] = base + (int64_t)rr * ld + koff[i];
       rs[i] = sgpr_rsrc(base + (int64_t)r0 * ld);
-      vo[i] = (uint32_t)((int64_t)(rr - r0) * ld) + (uint32_t)koff[i];
+      vo[i] = (uint32_t)((int64_t)(rr - r0) * ld) + (uint32_t)koff;
     }
   }
 
@@ -339,35 +334,75 @@ struct DmaPlan {
   __device__ __forceinline__ void issue(uint32_t slot, int kb, int K, int w) const {
     if (kb + kChunk <= K) {
 #pragma unroll
-      for (int i = 0; i < DPS; ++i) dma16_buf(vo[i], rs[i], kb, slot + (uint32_t)((i * 4 + w) * 1024));
+      for (int i = 0; i < DPS; ++i) dma16_buf(vo[i], rs[i], kb, slot + (uint32_t)((i * NW + w) * 1024));
     } else {
 #pragma unroll
       for (int i = 0; i < DPS; ++i) {
-        const void* p = kb + koff[i] < K ? (const void*)(src[i] + kb) : (const void*)g_zero16;
-        dma16(p, slot + (uint32_t)((i * 4 + w) * 1024));
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(
+            ((uint64_t)(uint32_t)rs[i][1] << 32) | (uint32_t)rs[i][0]);
+        const void* p = kb + koff < K ? (const void*)(base + vo[i] + kb) : (const void*)g_zero16;
+        dma16(p, slot + (uint32_t)((i * NW + w) * 1024));
       }
     }
   }
 };
 
+// Wait until at most `after` ring stages (DPS copies each) issued behind the
+// one about to be read are still in flight (0 <= after <= MAXA).
+template <int DPS, int MAXA>
+__device__ __forceinline__ void wait_stages(int after) {
+  if constexpr (MAXA >= 4) {
+    if (after >= 4) {
+      wait_vmcnt<4 * DPS>();
+      return;
+    }
+  }
+  if constexpr (MAXA >= 3) {
+    if (after == 3) {
+      wait_vmcnt<3 * DPS>();
+      return;
+    }
+  }
+  if constexpr (MAXA >= 2) {
+    if (after == 2) {
+      wait_vmcnt<2 * DPS>();
+      return;
+    }
+  }
+  if (after == 1)
+    wait_vmcnt<DPS>();
+  else
+    wait_vmcnt<0>();
+}
+
 // ---------------------------------------------------------------------------
-// Rowwise tile kernel: BM x BN workgroup tile, 4 wavefronts in a 2 x 2 grid
-// (wave tile BM/2 x BN/2), 64-wide K chunks in an NSLOT-slot LDS ring filled
-// by global->LDS DMA NSLOT-1 chunks ahead, one barrier per chunk.  OCC is the
-// number of workgroups meant to share a CU (their waits hide each other's).
-template <int BM, int BN, int NSLOT, int OCC, int EPI>
-__global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
+// Rowwise tile kernel: BM x BN workgroup tile, WM x WN wavefronts of 64 x 64
+// outputs (2 x 2 subtiles of 32 x 32), 64-wide K chunks in an NSLOT-slot LDS
+// ring filled by global->LDS DMA, one barrier per chunk.  Software
+// pipelined: the barrier that makes chunk k + 1 visible comes before chunk
+// k's matrix work, chunk k + 1's fragments are read right after it (into a
+// second register set) while chunk k is multiplied from registers; chunk k's
+// slot is then free (every wavefront holds its fragments) and takes the copy
+// of chunk k + NSLOT.  Each output keeps a block partial and a master (two
+// fp32 registers), which is what bounds a wavefront's tile at 64 x 64 with
+// two wavefronts per SIMD.  OCC is the number of workgroups meant to share a
+// CU (their waits hide each other's).
+template <int BM, int BN, int WM, int WN, int NSLOT, int OCC, int EPI>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_rowwise_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
     int sa_vec, const float* __restrict__ sb, int sb_vec, const uint16_t* __restrict__ bias,
     int tiles_m, int tiles_n, GemmBatch gb) {
-  constexpr int TM = BM / 32, TN = BN / 32;
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   constexpr int ROWS = BM + BN;
   constexpr int SLOT = ROWS * kChunk;          // bytes per ring slot
   constexpr int SEGS = SLOT / 1024;            // 1 KB segments per slot (16 rows each)
-  constexpr int DPS = SEGS / 4;                // DMA instructions per thread per stage
-  static_assert(NSLOT >= 2 && NSLOT <= 4, "ring depth");
-  static_assert(SEGS % 4 == 0, "segments must split over the four wavefronts");
+  constexpr int DPS = SEGS / NW;               // DMA instructions per thread per stage
+  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wavefront tiles of 32 x 32 subtiles");
+  static_assert(NSLOT >= 2 && NSLOT <= 6, "ring depth");
+  static_assert(SEGS % NW == 0, "segments must split over the wavefronts");
+  static_assert(kBlockChunks % 2 == 0, "fragment sets alternate by chunk parity");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NSLOT * SLOT];
 
   int tm, tn;
@@ -385,64 +420,97 @@ __global__ __launch_bounds__(256, OCC) void gemm_rowwise_kernel(
   }
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = w >> 1, wn = w & 1;
-  const int g = lane >> 4, r16 = lane & 15;
+  const int wm = w / WN, wn = w % WN;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
 
-  DmaPlan<DPS, BM> dma;
+  DmaPlan<DPS, BM, NW> dma;
   dma.init(A, lda, B, ldb, m0, n0, M, N, w, lane);
   const int nkc = (K + kChunk - 1) / kChunk;
   auto issue = [&](int kc) {
     dma.issue(lds0 + (uint32_t)((kc % NSLOT) * SLOT), kc * kChunk, K, w);
   };
 
-  // fragment read offsets (bytes within a slot)
-  const int a_off = (wm * (BM / 2) + r16) * kChunk + ((g ^ swz16(r16)) << 4);
-  const int b_off = (BM + wn * (BN / 2) + r16) * kChunk + ((g ^ swz16(r16)) << 4);
+  // fragment read offsets (bytes within a slot): two 16-byte pieces per row
+  const int a_off0 = wm * (BM / WM) * kChunk + frag32_off(lane, 0);
+  const int a_off1 = wm * (BM / WM) * kChunk + frag32_off(lane, 1);
+  const int b_off0 = (BM + wn * (BN / WN)) * kChunk + frag32_off(lane, 0);
+  const int b_off1 = (BM + wn * (BN / WN)) * kChunk + frag32_off(lane, 1);
+  auto read_frags = [&](int kc, Frag32 (&fa)[TM], Frag32 (&fb)[TN]) {
+    const uint8_t* slot = lds + (kc % NSLOT) * SLOT;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      fa[i].q[0] = *reinterpret_cast<const uint4*>(slot + a_off0 + i * 32 * kChunk);
+      fa[i].q[1] = *reinterpret_cast<const uint4*>(slot + a_off1 + i * 32 * kChunk);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      fb[j].q[0] = *reinterpret_cast<const uint4*>(slot + b_off0 + j * 32 * kChunk);
+      fb[j].q[1] = *reinterpret_cast<const uint4*>(slot + b_off1 + j * 32 * kChunk);
+    }
+  };
 
-  f32x4 acc[TM][TN];
+  f32x16 acc[TM][TN], mast[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc[i][j][v] = 0.f;
+        mast[i][j][v] = 0.f;
+      }
+  const float one[TM] = {};  // unused scale operand of the unscaled widen
 
+  Frag32 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
   for (int c = 0; c < NSLOT - 1 && c < nkc; ++c) issue(c);
-  for (int kc = 0; kc < nkc; ++kc) {
-    // stages issued behind chunk kc and still allowed in flight
-    const int after = min(NSLOT - 2, nkc - 1 - kc);
-    if (after >= 2)
-      wait_vmcnt<2 * DPS>();
-    else if (after == 1)
-      wait_vmcnt<DPS>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();  // chunk kc visible to all; slot of chunk kc-1 free
-    if (kc + NSLOT - 1 < nkc) issue(kc + NSLOT - 1);
-    const uint8_t* slot = lds + (kc % NSLOT) * SLOT;
-    uint4 fa[TM], fb[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const uint4*>(slot + a_off + i * 16 * kChunk);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const uint4*>(slot + b_off + j * 16 * kChunk);
-    // The widen + matrix phase runs at raised wave priority: the SIMD's other
-    // wavefront (another workgroup, in its barrier / copy / fragment-read
-    // phase) then fills the issue slots the matrix instructions leave, rather
-    // than delaying them (measured: QKV shape 1464 -> 1380 us).
-    __builtin_amdgcn_s_setprio(1);
-    mma_chunk64_bt<TM, TN>(fa, fb, acc);
-    __builtin_amdgcn_s_setprio(0);
+  wait_stages<DPS, NSLOT - 2>(min(NSLOT - 2, nkc - 1));
+  __syncthreads();  // chunk 0 visible
+  if (NSLOT - 1 < nkc) issue(NSLOT - 1);
+  read_frags(0, fa0, fb0);
+  // chunk kc, whose fragments are in (fa, fb): make chunk kc + 1 visible,
+  // start reading it into (na, nb), queue the copy of chunk kc + NSLOT into
+  // chunk kc's slot, multiply chunk kc (FRESH: it opens a block)
+  auto step = [&](int kc, auto fresh, const Frag32 (&fa)[TM], const Frag32 (&fb)[TN],
+                  Frag32 (&na)[TM], Frag32 (&nb)[TN]) {
+    constexpr bool F = decltype(fresh)::value;
+    if (kc + 1 < nkc) {
+      wait_stages<DPS, NSLOT - 2>(min(NSLOT - 2, nkc - 2 - kc));
+      __syncthreads();
+      if (kc + NSLOT < nkc) issue(kc + NSLOT);
+      read_frags(kc + 1, na, nb);
+    }
+    mma32_chunk<TM, TN, false, F>(fa, one, fb, acc);
+  };
+  // blocks of kBlockChunks chunks; chunk kc uses fragment set kc % 2
+  for (int kb = 0; kb < nkc; kb += kBlockChunks) {
+    const int kend = min(kb + kBlockChunks, nkc);
+    step(kb, std::true_type{}, fa0, fb0, fa1, fb1);
+    int kc = kb + 1;
+    for (; kc + 1 < kend; kc += 2) {
+      step(kc, std::false_type{}, fa1, fb1, fa0, fb0);
+      step(kc + 1, std::false_type{}, fa0, fb0, fa1, fb1);
+    }
+    if (kc < kend) step(kc, std::false_type{}, fa1, fb1, fa0, fb0);
+    promote_block<TM, TN>(acc, mast);
   }
 
+  // lane l holds output row l % 32 of each row subtile and the columns
+  // 8v + 4(l / 32) .. +3 of each column subtile in mast[.][.][4v .. 4v + 3]
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int r = m0 + wm * (BM / 2) + 16 * i + r16;
+    const int r = m0 + wm * (BM / WM) + 32 * i + (lane & 31);
     if (r >= M) continue;
     const float sar = sa[sa_vec ? r : 0];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int c = n0 + wn * (BN / 2) + 16 * j + 4 * g;
-      if (c < N) store_row4<EPI>(C, ldc, r, c, acc[i][j], sar, sb, sb_vec, bias);
-    }
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = n0 + wn * (BN / WN) + 32 * j + 8 * v + 4 * (lane >> 5);
+        if (c >= N) continue;
+        const f32x4 a4 = {mast[i][j][4 * v], mast[i][j][4 * v + 1], mast[i][j][4 * v + 2],
+                          mast[i][j][4 * v + 3]};
+        store_row4<EPI>(C, ldc, r, c, a4, sar, sb, sb_vec, bias);
+      }
   }
 }
 
@@ -740,21 +808,36 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel (M <= 16 * TM): one wavefront owns 16 output columns and walks
-// all of K in the canonical order, streaming A and B straight into registers
-// D chunks ahead (software pipelined: chunk c + D is requested while chunk c
-// is multiplied).  The nf = K / 64 whole chunks are loaded branch-free from a
-// wave-uniform base plus a 32-bit lane offset (requests past chunk nf - 1
-// re-read it and are never used), so the compiler's wait counts keep the D
-// chunks in flight.  A partial last chunk is loaded on its own: a lane's 16
-// bytes past K are read from the row's last 16 bytes, and its A values there
-// are zeroed before the multiply (B's duplicates then meet zeros).
-template <int TM, int D, int EPI>
-__global__ __launch_bounds__(64) void gemm_decode_kernel(
+// Decode kernel (M <= 32 * TMD): a workgroup of NWD wavefronts owns 32 output
+// columns.  Wavefront w computes the canonical blocks w, w + NWD, ... of K,
+// each a fresh partial chained through its chunks, streamed straight from
+// global memory into registers one block ahead (no LDS for the operands).
+// After each round of NWD blocks the partials meet in LDS and wavefront 0
+// adds them to its master in ascending block order: the same fp32 operations
+// in the same order as the tile kernels, so every row is bitwise identical
+// to theirs, while the wavefronts' chains run side by side.
+//
+// The round's work is branch-free (a branch around loads would make the
+// compiler wait for every outstanding load at its join, which defeats the
+// prefetch): a chunk slot the wavefront does not own this round is
+// multiplied with its A operand zeroed, which adds exactly +0 to the
+// partial.  Whole chunks are loaded from a wave-uniform base (scalar
+// registers) plus a 32-bit lane offset; a slot past the wavefront's last
+// chunk re-reads a valid chunk (with REFILL: K has more blocks than the
+// workgroup has wavefronts, so there is a next round to load).  With PART
+// (K % 64 != 0) the chunk past the
+// whole chunks is loaded after every round's slots from clamped addresses
+// (pieces past K re-read the row's last 16 bytes) and multiplied, its A
+// values past K -- and all of them outside the block that owns that chunk --
+// zeroed.
+template <int TMD, int NWD, bool PART, bool REFILL, int EPI>
+__global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
     int sa_vec, const float* __restrict__ sb, int sb_vec, const uint16_t* __restrict__ bias,
     GemmBatch gb) {
+  constexpr int D = kBlockChunks;
+  __shared__ f32x16 part[NWD][TMD][64];
   {
     const int64_t bi = blockIdx.y;
     A += bi * gb.a;
@@ -763,90 +846,125 @@ __global__ __launch_bounds__(64) void gemm_decode_kernel(
     sa += bi * gb.sa;
     sb += bi * gb.sb;
     M = (int)batch_rows(gb.rows, M);
-    if (M == 0) return;
+    if (M == 0) return;  // the whole workgroup, before any barrier
   }
-  const int lane = threadIdx.x;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int n0 = blockIdx.x * 16;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int n0 = blockIdx.x * 32;
   const int nf = K / kChunk;  // whole chunks
-  const int kl = 16 * g;
-  // byte offsets within a 16-row panel (rows past N / M repeat the last row);
-  // 16 * max(lda, ldb) stays far below 2^32 for K <= 65536 and 16-byte rows
-  const uint32_t bo = (uint32_t)(min(r16, N - 1 - n0) * ldb + kl);
-  const uint8_t* bbase = B + (int64_t)n0 * ldb;
-  uint32_t ao[TM];
+  const int nkc = (K + kChunk - 1) / kChunk;
+  const int nblk = (nkc + D - 1) / D;
+  // row byte offsets (rows past N / M repeat the last row); 64 rows of at
+  // most 2^24 bytes keep them below 2^31
+  const uint32_t brow = (uint32_t)(min(r32, N - 1 - n0) * ldb);
+  uint32_t arow[TMD];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) ao[i] = (uint32_t)(min(16 * i + r16, M - 1) * lda + kl);
-  // Buffer loads: the wave-uniform panel base and the chunk offset stay in
-  // scalar registers, so a load costs no vector address arithmetic (offsets
-  // are below 2^31: K <= 65536 and 64 rows of at most 64 KiB; the record
-  // count never clamps).
+  for (int i = 0; i < TMD; ++i) arow[i] = (uint32_t)(min(32 * i + r32, M - 1) * lda);
+  const uint8_t* bbase = B + (int64_t)n0 * ldb;
   const __amdgpu_buffer_rsrc_t rsb =
       __builtin_amdgcn_make_buffer_rsrc((void*)bbase, (short)0, 0x7FFFFFFF, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0x7FFFFFFF, kBufferWord3);
-  auto ldb16 = [&](int kc) -> uint4 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsb, (int)bo, kc * kChunk, 0);
+  auto ld16 = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, int soff) -> uint4 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, soff, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
   };
-  auto lda16 = [&](int i, int kc) -> uint4 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsa, (int)ao[i], kc * kChunk, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-  };
-  f32x4 acc[TM][1];
+  auto load_chunk = [&](int kc, Frag32& fb, Frag32 (&fa)[TMD]) {
+    fb.q[0] = ld16(rsb, brow + 32 * h, kc * kChunk);
+    fb.q[1] = ld16(rsb, brow + 32 * h + 16, kc * kChunk);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) acc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const uint4& fbv, const uint4 (&fa)[TM]) {
-    const uint4 fb[1] = {fbv};
-    mma_chunk64<TM, 1>(fa, fb, acc);
-  };
-  if (nf > 0) {
-    uint4 rb[D], ra[D][TM];
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int kc = min(d, nf - 1);
-      rb[d] = ldb16(kc);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) ra[d][i] = lda16(i, kc);
+    for (int i = 0; i < TMD; ++i) {
+      fa[i].q[0] = ld16(rsa, arow[i] + 32 * h, kc * kChunk);
+      fa[i].q[1] = ld16(rsa, arow[i] + 32 * h + 16, kc * kChunk);
     }
-    int kc0 = 0;
-    for (; kc0 + D <= nf; kc0 += D) {
+  };
+  // whole chunk of the wave's t-th chunk slot: position t % D of block
+  // w + NWD (t / D), clamped into the whole chunks
+  auto chunk_of = [&](int t) { return min((w + NWD * (t / D)) * D + t % D, nf - 1); };
+  const float one[TMD] = {};
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+
+  f32x16 mast[TMD][1], acc[TMD][1];
+#pragma unroll
+  for (int i = 0; i < TMD; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mast[i][0][v] = 0.f;
+  Frag32 rb[D], ra[D][TMD];
+  if (nf > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_chunk(chunk_of(d), rb[d], ra[d]);
+  }
+  // the chunk past the whole chunks, at clamped offsets
+  const int kpart = nf * kChunk + 32 * h;
+  const int poff0 = min(kpart, K - 16), poff1 = min(kpart + 16, K - 16);
+  for (int r = 0; r < nblk; r += NWD) {
+    const int blk = r + w;
+#pragma unroll
+    for (int i = 0; i < TMD; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][0][v] = 0.f;
+    if (nf > 0) {
+      const int nwhole = max(0, min(D, nf - blk * D));  // 0 when blk >= nblk
+      const int tnext = (r / NWD + 1) * D;             // the wave's next round
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        mma(rb[d], ra[d]);
-        const int kc = min(kc0 + d + D, nf - 1);
-        rb[d] = ldb16(kc);
+        const bool own = d < nwhole;
+        Frag32 fa[TMD];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) ra[d][i] = lda16(i, kc);
+        for (int i = 0; i < TMD; ++i) {
+          fa[i].q[0] = own ? ra[d][i].q[0] : z4;
+          fa[i].q[1] = own ? ra[d][i].q[1] : z4;
+        }
+        const Frag32 fb[1] = {rb[d]};
+        mma32_chunk<TMD, 1, false>(fa, one, fb, acc);
+        if constexpr (REFILL) load_chunk(chunk_of(tnext + d), rb[d], ra[d]);
       }
     }
+    if constexpr (PART) {
+      const bool own = blk == nf / D;
+      Frag32 pb[1], pa[TMD];
+      pb[0].q[0] = ld16(rsb, brow + (uint32_t)poff0, 0);
+      pb[0].q[1] = ld16(rsb, brow + (uint32_t)poff1, 0);
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (kc0 + d < nf) mma(rb[d], ra[d]);
-  }
-  if (nf * kChunk < K) {  // partial last chunk
-    const bool in = nf * kChunk + kl < K;
-    const int64_t shift = in ? 0 : (int64_t)(K - 16) - (nf * kChunk + kl);  // to the row's last 16 bytes
-    const uint4 fb = *reinterpret_cast<const uint4*>(bbase + (int64_t)nf * kChunk + bo + shift);
-    uint4 fa[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4*>(A + (int64_t)nf * kChunk + ao[i] + shift);
-      fa[i] = in ? v : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < TMD; ++i) {
+        const uint4 v0 = ld16(rsa, arow[i] + (uint32_t)poff0, 0);
+        const uint4 v1 = ld16(rsa, arow[i] + (uint32_t)poff1, 0);
+        pa[i].q[0] = own && kpart < K ? v0 : z4;
+        pa[i].q[1] = own && kpart + 16 < K ? v1 : z4;
+      }
+      mma32_chunk<TMD, 1, false>(pa, one, pb, acc);
     }
-    mma(fb, fa);
-  }
-  const int c = n0 + r16;
-  if (c >= N) return;
-  const float sbc = sb[sb_vec ? c : 0];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TMD; ++i) part[w][i][lane] = acc[i][0];
+    __syncthreads();
+    if (w == 0) {
+      for (int b = 0; b < NWD && r + b < nblk; ++b)
+#pragma unroll
+        for (int i = 0; i < TMD; ++i) {
+          const f32x16 p = part[b][i][lane];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mast[i][0][v] = mast[i][0][v] + p[v];
+        }
+    }
+    __syncthreads();
+  }
+  if (w != 0) return;
+  // lane l holds output row 32i + l % 32 and the columns 8v + 4(l / 32) .. +3
+#pragma unroll
+  for (int i = 0; i < TMD; ++i) {
+    const int rr = 32 * i + r32;
+    if (rr >= M) continue;
+    const float sar = sa[sa_vec ? rr : 0];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int r = 16 * i + 4 * g + v;
-      if (r < M)
-        C[(int64_t)r * ldc + c] = epi_round<EPI>(epi_value<EPI>(acc[i][0][v], sa[sa_vec ? r : 0], sbc, bias, c));
+      const int c = n0 + 8 * v + 4 * h;
+      if (c >= N) continue;
+      const f32x4 a4 = {mast[i][0][4 * v], mast[i][0][4 * v + 1], mast[i][0][4 * v + 2],
+                        mast[i][0][4 * v + 3]};
+      store_row4<EPI>(C, ldc, rr, c, a4, sar, sb, sb_vec, bias);
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -993,11 +1111,9 @@ __global__ void fill_k0_kernel(uint16_t* C, int64_t ldc, int64_t M, int64_t N,
 
 const char* variant_name(int v) {
   switch (v) {
-    case VAR_TILE_256x256: return "tile256x256";
-    case VAR_TILE_256x128: return "tile256x128";
     case VAR_TILE_128x128: return "tile128x128";
     case VAR_TILE_128x256: return "tile128x256";
-    case VAR_DECODE_16: return "decode16";
+    case VAR_TILE_256x128: return "tile256x128";
     case VAR_DECODE_32: return "decode32";
     case VAR_DECODE_64: return "decode64";
     default: return "unknown";
@@ -1006,11 +1122,9 @@ const char* variant_name(int v) {
 
 bool variant_accepts(int v, int64_t M) {
   switch (v) {
-    case VAR_TILE_256x256:
-    case VAR_TILE_256x128:
     case VAR_TILE_128x128:
-    case VAR_TILE_128x256: return true;
-    case VAR_DECODE_16: return M <= 16;
+    case VAR_TILE_128x256:
+    case VAR_TILE_256x128: return true;
     case VAR_DECODE_32: return M <= 32;
     case VAR_DECODE_64: return M <= 64;
     default: return false;
@@ -1033,41 +1147,49 @@ static hipError_t with_epi(const GemmArgs& g, Fn&& f) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int NSLOT, int OCC>
+template <int BM, int BN, int WM, int WN, int NSLOT, int OCC>
 static hipError_t launch_rowwise_tile(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
   return with_epi(g, [&](auto e) {
     constexpr int EPI = decltype(e)::value;
-    hipLaunchKernelGGL((gemm_rowwise_kernel<BM, BN, NSLOT, OCC, EPI>), grid2(tiles_m * tiles_n, g),
-                       dim3(256), 0, s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N,
+    hipLaunchKernelGGL((gemm_rowwise_kernel<BM, BN, WM, WN, NSLOT, OCC, EPI>),
+                       grid2(tiles_m * tiles_n, g), dim3(64 * WM * WN), 0, s, g.A, g.lda, g.B,
+                       g.ldb, g.C, g.ldc, (int)g.M, (int)g.N,
                        (int)g.K, static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
                        static_cast<const float*>(g.sb), (int)(g.sb_kind == 2),
                        static_cast<const uint16_t*>(g.bias), tiles_m, tiles_n, g.batch);
   });
 }
 
-template <int TM, int D>
+template <int TMD, int NWD>
 static hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
-  const int grid = (int)((g.N + 15) / 16);
-  return with_epi(g, [&](auto e) {
-    constexpr int EPI = decltype(e)::value;
-    hipLaunchKernelGGL((gemm_decode_kernel<TM, D, EPI>), grid2(grid, g), dim3(64), 0, s, g.A,
-                       g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K,
-                       static_cast<const float*>(g.sa), (int)(g.sa_kind == 1),
-                       static_cast<const float*>(g.sb), (int)(g.sb_kind == 2),
-                       static_cast<const uint16_t*>(g.bias), g.batch);
-  });
+  const int grid = (int)((g.N + 31) / 32);
+  const int64_t nblk = (g.K + kChunk * kBlockChunks - 1) / (kChunk * kBlockChunks);
+  auto go = [&](auto part, auto refill) {
+    return with_epi(g, [&](auto e) {
+      constexpr int EPI = decltype(e)::value;
+      constexpr bool PART = decltype(part)::value, REFILL = decltype(refill)::value;
+      hipLaunchKernelGGL((gemm_decode_kernel<TMD, NWD, PART, REFILL, EPI>), grid2(grid, g),
+                         dim3(64 * NWD), 0, s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M,
+                         (int)g.N, (int)g.K, static_cast<const float*>(g.sa),
+                         (int)(g.sa_kind == 1), static_cast<const float*>(g.sb),
+                         (int)(g.sb_kind == 2), static_cast<const uint16_t*>(g.bias), g.batch);
+    });
+  };
+  if (nblk > NWD)
+    return g.K % kChunk ? go(std::true_type{}, std::true_type{})
+                        : go(std::false_type{}, std::true_type{});
+  return g.K % kChunk ? go(std::true_type{}, std::false_type{})
+                      : go(std::false_type{}, std::false_type{});
 }
 
 hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
   switch (variant) {
-    case VAR_TILE_256x256: return launch_rowwise_tile<256, 256, 4, 1>(g, s);
-    case VAR_TILE_256x128: return launch_rowwise_tile<256, 128, 3, 2>(g, s);
-    case VAR_TILE_128x128: return launch_rowwise_tile<128, 128, 4, 2>(g, s);
-    case VAR_TILE_128x256: return launch_rowwise_tile<128, 256, 3, 2>(g, s);
-    case VAR_DECODE_16: return launch_decode<1, 24>(g, s);
-    case VAR_DECODE_32: return launch_decode<2, 12>(g, s);
-    case VAR_DECODE_64: return launch_decode<4, 8>(g, s);
+    case VAR_TILE_128x128: return launch_rowwise_tile<128, 128, 2, 2, 4, 2>(g, s);
+    case VAR_TILE_128x256: return launch_rowwise_tile<128, 256, 2, 4, 4, 1>(g, s);
+    case VAR_TILE_256x128: return launch_rowwise_tile<256, 128, 4, 2, 4, 1>(g, s);
+    case VAR_DECODE_32: return launch_decode<1, 8>(g, s);
+    case VAR_DECODE_64: return launch_decode<2, 4>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

