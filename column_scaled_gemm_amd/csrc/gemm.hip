@@ -810,33 +810,44 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 32 * TMD): a workgroup of NWD wavefronts owns 32 output
 // columns.  Wavefront w computes the canonical blocks w, w + NWD, ... of K,
-// each a fresh partial chained through its chunks, streamed straight from
-// global memory into registers one block ahead (no LDS for the operands).
-// After each round of NWD blocks the partials meet in LDS and wavefront 0
-// adds them to its master in ascending block order: the same fp32 operations
-// in the same order as the tile kernels, so every row is bitwise identical
-// to theirs, while the wavefronts' chains run side by side.
+// each a fresh partial chained through its chunks; after each round of NWD
+// blocks the partials meet in LDS and wavefront 0 adds them to its master in
+// ascending block order: the same fp32 operations in the same order as the
+// tile kernels, so every row is bitwise identical to theirs, while the
+// wavefronts' chains run side by side.
 //
-// The round's work is branch-free (a branch around loads would make the
-// compiler wait for every outstanding load at its join, which defeats the
-// prefetch): a chunk slot the wavefront does not own this round is
-// multiplied with its A operand zeroed, which adds exactly +0 to the
-// partial.  Whole chunks are loaded from a wave-uniform base (scalar
-// registers) plus a 32-bit lane offset; a slot past the wavefront's last
-// chunk re-reads a valid chunk (with REFILL: K has more blocks than the
-// workgroup has wavefronts, so there is a next round to load).  With PART
-// (K % 64 != 0) the chunk past the
-// whole chunks is loaded after every round's slots from clamped addresses
-// (pieces past K re-read the row's last 16 bytes) and multiplied, its A
-// values past K -- and all of them outside the block that owns that chunk --
-// zeroed.
-template <int TMD, int NWD, bool PART, bool REFILL, int EPI>
+// The weight block (32 rows x 512 bytes) is what streams from HBM.  It is
+// copied by global->LDS DMA into the wavefront's own LDS region, each copy
+// instruction taking two whole 512-byte rows (every cache line it touches is
+// used whole), and read back in the matrix layout; no other wavefront reads
+// the region, so waiting for the wavefront's own copies is enough (no
+// barrier).  Within a row, 16-byte piece p sits at position p ^ (row % 16),
+// so each 16-lane phase of a fragment read hits 16 distinct bank groups.  The
+// copies of a wavefront's next block are issued as soon as the current
+// block's fragments are in registers, so they overlap its chain.  The few A
+// rows (L2-resident, shared by every workgroup) are read straight into
+// registers.
+//
+// A chunk slot past the wavefront's whole chunks (its block is the last one
+// and partial, or it has no block this round) is multiplied with its A
+// operand zeroed, which adds exactly +0 to a partial that started at +0; its
+// copies re-read the row's first bytes, so no copy leaves the row.  With
+// PART (K % 64 != 0) the chunk past the whole chunks is loaded from clamped
+// addresses (pieces past K re-read the row's last 16 bytes) and multiplied
+// with its A values past K -- and all of them outside the block that owns
+// that chunk -- zeroed.
+template <int TMD, int NWD, bool PART, int EPI>
 __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
     int sa_vec, const float* __restrict__ sb, int sb_vec, const uint16_t* __restrict__ bias,
     GemmBatch gb) {
   constexpr int D = kBlockChunks;
+  constexpr int RB = D * kChunk;   // bytes of a block row (512)
+  constexpr int REG = 32 * RB;     // a wavefront's LDS region: 32 rows of a block
+  constexpr int NCP = REG / 1024;  // copy instructions per block (two rows each)
+  static_assert(RB == 512, "two block rows per 64-lane copy of 16 bytes each");
+  __shared__ __attribute__((aligned(1024))) uint8_t bls[NWD * REG];
   __shared__ f32x16 part[NWD][TMD][64];
   {
     const int64_t bi = blockIdx.y;
@@ -855,35 +866,64 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
   const int nf = K / kChunk;  // whole chunks
   const int nkc = (K + kChunk - 1) / kChunk;
   const int nblk = (nkc + D - 1) / D;
-  // row byte offsets (rows past N / M repeat the last row); 64 rows of at
-  // most 2^24 bytes keep them below 2^31
-  const uint32_t brow = (uint32_t)(min(r32, N - 1 - n0) * ldb);
+  const int last = N - 1 - n0;  // B rows past N repeat the last row
+
+  // copy instruction j fills rows 2j, 2j + 1 of the region: lane l copies
+  // row 2j + l / 32, logical piece (l % 32) ^ (row % 16) into position l % 32.
+  // Row offsets stay below 2^31 (32 rows of at most 2^24 bytes, plus K).
+  const uint8_t* bbase = B + (int64_t)n0 * ldb;
+  const i32x4 rsb = sgpr_rsrc(bbase);
+  const uint32_t region =
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)bls) + (uint32_t)(w * REG);
+  auto issue_block = [&](int blk) {
+    const int kwhole = nf * kChunk;
+#pragma unroll
+    for (int j = 0; j < NCP; ++j) {
+      const int row = min(2 * j + h, last);
+      const int kp = blk * RB + 16 * (r32 ^ (row & 15));
+      const uint32_t off = (uint32_t)(row * ldb) + (uint32_t)(kp + 16 <= kwhole ? kp : 0);
+      dma16_buf(off, rsb, 0, region + (uint32_t)(j * 1024));
+    }
+  };
+  // fragment reads: row r32 of the region, logical pieces 4d + 2h + q
+  const uint8_t* myrow = bls + w * REG + r32 * RB;
+  auto read_b = [&](Frag32 (&rb)[D]) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      rb[d].q[0] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h) ^ (r32 & 15)));
+      rb[d].q[1] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h + 1) ^ (r32 & 15)));
+    }
+  };
+
   uint32_t arow[TMD];
 #pragma unroll
   for (int i = 0; i < TMD; ++i) arow[i] = (uint32_t)(min(32 * i + r32, M - 1) * lda);
-  const uint8_t* bbase = B + (int64_t)n0 * ldb;
-  const __amdgpu_buffer_rsrc_t rsb =
-      __builtin_amdgcn_make_buffer_rsrc((void*)bbase, (short)0, 0x7FFFFFFF, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0x7FFFFFFF, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsbv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)bbase, (short)0, 0x7FFFFFFF, kBufferWord3);
   auto ld16 = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, int soff) -> uint4 {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, soff, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
   };
-  auto load_chunk = [&](int kc, Frag32& fb, Frag32 (&fa)[TMD]) {
-    fb.q[0] = ld16(rsb, brow + 32 * h, kc * kChunk);
-    fb.q[1] = ld16(rsb, brow + 32 * h + 16, kc * kChunk);
+  // A chunks of block blk (clamped into the whole chunks; masked where used)
+  auto load_a = [&](int blk, Frag32 (&ra)[D][TMD]) {
 #pragma unroll
-    for (int i = 0; i < TMD; ++i) {
-      fa[i].q[0] = ld16(rsa, arow[i] + 32 * h, kc * kChunk);
-      fa[i].q[1] = ld16(rsa, arow[i] + 32 * h + 16, kc * kChunk);
+    for (int d = 0; d < D; ++d) {
+      const int kc = min(blk * D + d, nf - 1);
+#pragma unroll
+      for (int i = 0; i < TMD; ++i) {
+        ra[d][i].q[0] = ld16(rsa, arow[i] + 32 * h, kc * kChunk);
+        ra[d][i].q[1] = ld16(rsa, arow[i] + 32 * h + 16, kc * kChunk);
+      }
     }
   };
-  // whole chunk of the wave's t-th chunk slot: position t % D of block
-  // w + NWD (t / D), clamped into the whole chunks
-  auto chunk_of = [&](int t) { return min((w + NWD * (t / D)) * D + t % D, nf - 1); };
   const float one[TMD] = {};
   const uint4 z4 = make_uint4(0, 0, 0, 0);
+  // the chunk past the whole chunks, at clamped offsets
+  const int kpart = nf * kChunk + 32 * h;
+  const int poff0 = min(kpart, K - 16), poff1 = min(kpart + 16, K - 16);
+  const uint32_t brow = (uint32_t)(min(r32, last) * ldb);
 
   f32x16 mast[TMD][1], acc[TMD][1];
 #pragma unroll
@@ -892,12 +932,9 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
     for (int v = 0; v < 16; ++v) mast[i][0][v] = 0.f;
   Frag32 rb[D], ra[D][TMD];
   if (nf > 0) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) load_chunk(chunk_of(d), rb[d], ra[d]);
+    issue_block(min(w, nblk - 1));
+    load_a(min(w, nblk - 1), ra);
   }
-  // the chunk past the whole chunks, at clamped offsets
-  const int kpart = nf * kChunk + 32 * h;
-  const int poff0 = min(kpart, K - 16), poff1 = min(kpart + 16, K - 16);
   for (int r = 0; r < nblk; r += NWD) {
     const int blk = r + w;
 #pragma unroll
@@ -905,8 +942,13 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][0][v] = 0.f;
     if (nf > 0) {
+      wait_vmcnt<0>();  // this round's copies and A loads
+      read_b(rb);
       const int nwhole = max(0, min(D, nf - blk * D));  // 0 when blk >= nblk
-      const int tnext = (r / NWD + 1) * D;             // the wave's next round
+      if (r + NWD < nblk) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region has been read
+        issue_block(min(blk + NWD, nblk - 1));
+      }
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const bool own = d < nwhole;
@@ -918,14 +960,14 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
         }
         const Frag32 fb[1] = {rb[d]};
         mma32_chunk<TMD, 1, false>(fa, one, fb, acc);
-        if constexpr (REFILL) load_chunk(chunk_of(tnext + d), rb[d], ra[d]);
       }
+      if (r + NWD < nblk) load_a(min(blk + NWD, nblk - 1), ra);
     }
     if constexpr (PART) {
       const bool own = blk == nf / D;
       Frag32 pb[1], pa[TMD];
-      pb[0].q[0] = ld16(rsb, brow + (uint32_t)poff0, 0);
-      pb[0].q[1] = ld16(rsb, brow + (uint32_t)poff1, 0);
+      pb[0].q[0] = ld16(rsbv, brow + (uint32_t)poff0, 0);
+      pb[0].q[1] = ld16(rsbv, brow + (uint32_t)poff1, 0);
 #pragma unroll
       for (int i = 0; i < TMD; ++i) {
         const uint4 v0 = ld16(rsa, arow[i] + (uint32_t)poff0, 0);
@@ -1116,6 +1158,7 @@ const char* variant_name(int v) {
     case VAR_TILE_256x128: return "tile256x128";
     case VAR_DECODE_32: return "decode32";
     case VAR_DECODE_64: return "decode64";
+    case VAR_DECODE_32_W4: return "decode32w4";
     default: return "unknown";
   }
 }
@@ -1125,7 +1168,8 @@ bool variant_accepts(int v, int64_t M) {
     case VAR_TILE_128x128:
     case VAR_TILE_128x256:
     case VAR_TILE_256x128: return true;
-    case VAR_DECODE_32: return M <= 32;
+    case VAR_DECODE_32:
+    case VAR_DECODE_32_W4: return M <= 32;
     case VAR_DECODE_64: return M <= 64;
     default: return false;
   }
@@ -1164,23 +1208,18 @@ static hipError_t launch_rowwise_tile(const GemmArgs& g, hipStream_t s) {
 template <int TMD, int NWD>
 static hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
   const int grid = (int)((g.N + 31) / 32);
-  const int64_t nblk = (g.K + kChunk * kBlockChunks - 1) / (kChunk * kBlockChunks);
-  auto go = [&](auto part, auto refill) {
+  auto go = [&](auto part) {
     return with_epi(g, [&](auto e) {
       constexpr int EPI = decltype(e)::value;
-      constexpr bool PART = decltype(part)::value, REFILL = decltype(refill)::value;
-      hipLaunchKernelGGL((gemm_decode_kernel<TMD, NWD, PART, REFILL, EPI>), grid2(grid, g),
+      constexpr bool PART = decltype(part)::value;
+      hipLaunchKernelGGL((gemm_decode_kernel<TMD, NWD, PART, EPI>), grid2(grid, g),
                          dim3(64 * NWD), 0, s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M,
                          (int)g.N, (int)g.K, static_cast<const float*>(g.sa),
                          (int)(g.sa_kind == 1), static_cast<const float*>(g.sb),
                          (int)(g.sb_kind == 2), static_cast<const uint16_t*>(g.bias), g.batch);
     });
   };
-  if (nblk > NWD)
-    return g.K % kChunk ? go(std::true_type{}, std::true_type{})
-                        : go(std::false_type{}, std::true_type{});
-  return g.K % kChunk ? go(std::true_type{}, std::false_type{})
-                      : go(std::false_type{}, std::false_type{});
+  return g.K % kChunk ? go(std::true_type{}) : go(std::false_type{});
 }
 
 hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
@@ -1190,6 +1229,7 @@ hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
     case VAR_TILE_256x128: return launch_rowwise_tile<256, 128, 4, 2, 4, 1>(g, s);
     case VAR_DECODE_32: return launch_decode<1, 8>(g, s);
     case VAR_DECODE_64: return launch_decode<2, 4>(g, s);
+    case VAR_DECODE_32_W4: return launch_decode<1, 4>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -104,9 +104,10 @@ enum Variant {
   VAR_TILE_128x128 = 0,  // 128x128 tiles, 4 wavefronts, two workgroups per CU
   VAR_TILE_128x256 = 1,  // 128x256 tiles, 8 wavefronts, one workgroup per CU
   VAR_TILE_256x128 = 2,  // 256x128 tiles, 8 wavefronts, one workgroup per CU
-  VAR_DECODE_32 = 3,     // M <= 32: four wavefronts per 32 columns, register-streamed
-  VAR_DECODE_64 = 4,     // M <= 64
-  VAR_COUNT = 5
+  VAR_DECODE_32 = 3,     // M <= 32: eight wavefronts per 32 columns, one 512-K block each
+  VAR_DECODE_64 = 4,     // M <= 64: four wavefronts per 32 columns
+  VAR_DECODE_32_W4 = 5,  // M <= 32: four wavefronts per 32 columns, two workgroups per CU
+  VAR_COUNT = 6
 };
 const char* variant_name(int v);
 bool variant_accepts(int v, int64_t M);
