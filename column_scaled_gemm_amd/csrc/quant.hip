@@ -25,6 +25,10 @@ namespace fp8sm {
 
 enum { FMT_FP32 = 0, FMT_UE8M0_FP32 = 1, FMT_UE8M0_BYTE = 2 };
 
+// Largest grid of the per-token kernels (workgroups); more rows than the grid
+// covers are walked by its wavefronts.
+constexpr int64_t kMaxRowBlocks = 1 << 20;
+
 template <int FMT>
 __device__ __forceinline__ float group_multiplier(float amax, float* scale_val, int* ebyte) {
   const float a = fmaxf(amax, kAmaxFloor);
@@ -336,27 +340,31 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
   SiluTable<F16>::load(tab, threadIdx.x, 1024);
   __syncthreads();
   const int64_t step = 16 * nw;
-  while (g0 < total) {
-    g0 += step;
+  // Two steps per iteration with one exit test: both halves always run (a
+  // step past the end loads clamped rows and stores nothing), so the loop
+  // has no early exit whose join would make the compiler drain every load in
+  // flight at the loop head.
+  for (; g0 < total; g0 += 2 * step) {
     fetch(b);
     convert(a);
-    if (g0 >= total) break;
-    g0 += step;
     fetch(a);
     convert(b);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last, unused prefetch
 }
 
 // ---------------------------------------------------------------------------
-// Per token, row kept in registers: persistent wavefronts walk the rows
-// (row, row + waves in the grid, ...), holding a row as NC 16-byte chunks per
+// Per token, row kept in registers: wavefronts walk the rows (row, row +
+// waves in the grid, ...; the host gives every row its own wavefront up to
+// kMaxRowBlocks workgroups, which measured faster from HBM than a grid of
+// resident wavefronts walking several rows), holding a row as NC 16-byte chunks per
 // lane (chunk c = lane + 64 i; the host picks the smallest listed NC with
 // 64 * NC * 8 >= K, so the last chunks of a lane may lie past the row end:
 // those read the row's last chunk and are masked out of the maximum and the
 // stores; chunks below NFULL, the next smaller listed NC, always lie inside
-// the row).  The next row's loads are issued before the current row is
-// reduced, quantized and stored, so every wave keeps one row in flight while
-// it writes the previous one.
+// the row).  When a wavefront has another row, its loads are issued before
+// the current row is reduced, quantized and stored.  Codes go out as
+// streaming (nontemporal) stores.
 template <bool F16, int NC, int NFULL, int FMT>
 __global__ __launch_bounds__(256) void quant_token_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld_x,
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
       const uint2 codes = to_e4m3_x8(y);
-      if (ok[i]) *reinterpret_cast<uint2*>(qr + (int64_t)cidx[i] * 8) = codes;
+      if (ok[i]) store_stream8(qr + (int64_t)cidx[i] * 8, codes);
     }
     if (lane == 0) store_scale<FMT>(scales, r, sval, eb);
   };
@@ -427,9 +435,10 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
   }
 }
 
-// Per token, long rows: the four wavefronts of a workgroup share a row, each
-// holding NCW 16-byte chunks per lane (chunk c = 64 w + lane + 256 i), with
-// the next row's quarter loaded while the current one is converted.  The row
+// Per token, long rows (K > 4096): the four wavefronts of a workgroup share a
+// row, each holding NCW 16-byte chunks per lane (chunk c = 64 w + lane +
+// 256 i); a workgroup per row (up to kMaxRowBlocks), a next row's quarter
+// loaded while the current one is converted, streaming code stores.  The row
 // maximum is exchanged through LDS (two slots, alternating by row, so one
 // barrier per row suffices); chunks past the row end are clamped and masked.
 template <bool F16, int NCW, int FMT>
@@ -484,7 +493,7 @@ __global__ __launch_bounds__(256) void quant_token_wg_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
       const uint2 codes = to_e4m3_x8(y);
-      if (ok[i]) *reinterpret_cast<uint2*>(qr + (int64_t)cidx[i] * 8) = codes;
+      if (ok[i]) store_stream8(qr + (int64_t)cidx[i] * 8, codes);
     }
     if (threadIdx.x == 0) store_scale<FMT>(scales, r, sval, eb);
   };
@@ -767,21 +776,6 @@ static unsigned persistent_blocks(int64_t work_per_block_units, int64_t units, i
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(need, share));
 }
 
-// Rows walked by `per_block` rows at a time per workgroup: when the last round
-// of rows would be less than half full, keep the number of rounds but spread
-// the rows evenly over fewer workgroups, so that round is not run by a few
-// workgroups alone (8320 rows on 4096 persistent wavefronts would leave 128
-// rows as a third round: 26.0 -> 24.9 us measured).  A fuller last round
-// keeps the whole grid, whose extra rows in flight are worth more.
-static unsigned balanced_blocks(unsigned blocks, int64_t rows, int64_t per_block) {
-  const int64_t units = (int64_t)blocks * per_block;
-  const int64_t tail = rows % units;
-  if (tail == 0 || 2 * tail >= units) return blocks;
-  const int64_t rounds = std::max<int64_t>(1, (rows + units - 1) / units);
-  const int64_t need = (rows + rounds - 1) / rounds;  // rows per round
-  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, (need + per_block - 1) / per_block));
-}
-
 static dim3 grid2(int64_t blocks, const QuantBatch& bt) {
   return dim3((unsigned)blocks, (unsigned)bt.count);
 }
@@ -840,17 +834,6 @@ static hipError_t launch_g128_fused(int fmt, const QuantArgs& a, hipStream_t s) 
   });
 }
 
-// Resident 256-thread workgroups per CU for a kernel, queried once.
-template <typename Kern>
-static int resident_blocks(Kern k, std::atomic<int>& cache) {
-  int n = cache.load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 256, 0) != hipSuccess || n <= 0) n = 1;
-    cache.store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 // NC chunks per lane; the caller guarantees the row has more than 64 * NFULL
 // chunks (so chunks below NFULL are whole).
 template <bool F16, int NC, int NFULL>
@@ -858,10 +841,7 @@ static hipError_t launch_token_nc(int fmt, const QuantArgs& a, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   return with_fmt(fmt, [&](auto f) {
     constexpr int FMT = decltype(f)::value;
-    static std::atomic<int> occ{0};
-    const int per_cu = resident_blocks(quant_token_kernel<F16, NC, NFULL, FMT>, occ);
-    const int64_t blocks = balanced_blocks(
-        persistent_blocks(4, a.M, a.batch.count, (int64_t)per_cu * cu_count()), a.M, 4);
+    const int64_t blocks = std::min<int64_t>((a.M + 3) / 4, kMaxRowBlocks);
     hipLaunchKernelGGL((quant_token_kernel<F16, NC, NFULL, FMT>), grid2(blocks, a.batch),
                        dim3(256), 0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.batch);
   });
@@ -893,10 +873,7 @@ static hipError_t launch_token_wg(int fmt, const QuantArgs& a, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   return with_fmt(fmt, [&](auto f) {
     constexpr int FMT = decltype(f)::value;
-    static std::atomic<int> occ{0};
-    const int per_cu = resident_blocks(quant_token_wg_kernel<F16, NCW, FMT>, occ);
-    const int64_t blocks = balanced_blocks(
-        persistent_blocks(1, a.M, a.batch.count, (int64_t)per_cu * cu_count()), a.M, 1);
+    const int64_t blocks = std::min<int64_t>(a.M, kMaxRowBlocks);
     hipLaunchKernelGGL((quant_token_wg_kernel<F16, NCW, FMT>), grid2(blocks, a.batch), dim3(256),
                        0, s, x, a.M, a.K, a.ld_x, a.q, a.ld_q, a.scales, a.batch);
   });
@@ -910,9 +887,8 @@ static hipError_t launch_token(int fmt, const QuantArgs& a, hipStream_t s) {
   if (per_lane <= 4) return launch_token_nc<F16, 4, 2>(fmt, a, s);
   if (per_lane <= 6) return launch_token_nc<F16, 6, 4>(fmt, a, s);
   if (per_lane <= 8) return launch_token_nc<F16, 8, 6>(fmt, a, s);
-  if (per_lane <= 11) return launch_token_nc<F16, 11, 8>(fmt, a, s);
-  if (per_lane <= 14) return launch_token_nc<F16, 14, 11>(fmt, a, s);
   const int64_t per_wave = (a.K / 8 + 255) / 256;  // chunks per lane with 4 waves per row
+  if (per_wave <= 3) return launch_token_wg<F16, 3>(fmt, a, s);
   if (per_wave <= 4) return launch_token_wg<F16, 4>(fmt, a, s);
   if (per_wave <= 6) return launch_token_wg<F16, 6>(fmt, a, s);
   if (per_wave <= 8) return launch_token_wg<F16, 8>(fmt, a, s);
