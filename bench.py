@@ -21,8 +21,9 @@ GEMM rows).
 
 Other modes: --suite (every hot-path kernel on its own workload), --sweep
 (every rowwise kernel variant over a grid of M and (N, K): the measurements
-the shape dispatch table is generated from), --copy-calibration (a plain copy
-of known size for scaling the traffic counters).
+the shape dispatch table is generated from), --ceilings (measured matrix-pipe
+and HBM ceilings), --copy-calibration (a plain copy of known size for scaling
+the traffic counters).
 """
 import argparse
 import json
@@ -40,11 +41,11 @@ PEAK_FP8_MFMA = 5000.0      # TFLOP/s, dense
 PEAK_HBM = 8000.0           # GB/s
 
 # HBM traffic of one QKV GEMM launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# passes, scaled by a plain-copy calibration (profiles/
-# gemm_rowwise_128x256_qkv_traffic.md).  Valid only for the gemm.hip source it
-# was measured on; reported as null once that file changes.
-TRAFFIC = {"gemm_src_sha256_prefix": "a73bf551d04ce3b2", "workload": "qkv",
-           "kernel": "tile128x256", "bytes": 1717.9e6 + 358.3e6}
+# passes, scaled by a plain-copy calibration (FETCH_SIZE x2, WRITE_SIZE x1;
+# profiles/gemm_rowwise_qkv_traffic.md).  Valid only for the gemm.hip source
+# and kernel variant it was measured on; reported as null once either changes.
+TRAFFIC = {"gemm_src_sha256_prefix": "112de6baf6456e93", "workload": "qkv",
+           "kernel": "tile128x128", "bytes": 3136.4e6 + 367.9e6}
 
 
 def measured_traffic(workload, variant):
@@ -76,6 +77,8 @@ def parse():
                    help="time every rowwise variant over the dispatch grid (one JSON line each)")
     p.add_argument("--sweep-out", default=None,
                    help="also write the sweep's lines to this file")
+    p.add_argument("--ceilings", action="store_true",
+                   help="measured matrix-pipe and HBM ceilings (one JSON line each)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB three times (a known-size "
                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -91,6 +94,80 @@ def copy_calibration(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "reads": n, "writes": n, "launches": 3}))
+
+
+def ceilings(repeats=5):
+    """Measured ceilings of the machine, one JSON line each: the matrix pipe
+    on the GEMMs' instruction and accumulator count (fp8sm_rate_probe at 1, 2
+    and 4 wavefronts per SIMD, without and with the widen feeding the
+    operands) and HBM (a 1 GiB copy and a 1 GiB read, caches evicted first
+    by the other buffer).  Each figure is the median over `repeats` launches
+    timed with HIP events."""
+    import numpy as np
+    import torch
+    from column_scaled_gemm_amd import fp8sm
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    iters = 20000
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(repeats):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(ts))
+
+    for widen in (0, 1):
+        for wpb in (4, 8, 16):
+            us = timed(lambda: fp8sm.rate_probe(widen, cus, wpb, iters))
+            flop = 2.0 * 32 * 32 * 16 * 4 * iters * cus * wpb
+            tf = flop / us / 1e6
+            print(json.dumps({"ceiling": "matrix pipe, v_mfma_f32_32x32x16_bf16, 4 accumulators/wavefront"
+                              + (", widen feeding the operands" if widen else ""),
+                              "waves_per_simd": wpb // 4, "us": round(us, 1),
+                              "TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_MFMA, 4)}),
+                  flush=True)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    other = torch.ones(n // 8, dtype=torch.int64, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def copy_cold():
+        torch.sum(other, dim=0, out=sink)   # evicts src / dst (1 GiB read)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3
+
+    def read_cold():
+        dst.copy_(src)                     # evicts `other`
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.sum(other, dim=0, out=sink)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3
+
+    for name, fn, nbytes in (("HBM copy (torch copy_, 1 GiB read + 1 GiB write)", copy_cold, 2 * n),
+                             ("HBM read (torch sum, 1 GiB)", read_cold, n)):
+        fn()
+        us = float(np.median([fn() for _ in range(repeats)]))
+        gbs = nbytes / us / 1e3
+        print(json.dumps({"ceiling": name, "us": round(us, 1), "GBps": round(gbs, 1),
+                          "frac_of_hbm_peak": round(gbs / PEAK_HBM, 4)}), flush=True)
 
 
 def cpu_baseline(w, M, N, K, target_s):
@@ -535,6 +612,9 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.ceilings:
+        ceilings()
         return
     import numpy as np
     import torch

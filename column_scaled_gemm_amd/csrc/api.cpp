@@ -438,6 +438,20 @@ fp8sm_status fp8sm_mfma_probe(int32_t instr, const uint32_t* a_regs, const uint3
   return launched(launch_mfma_probe(instr, a_regs, b_regs, d_regs, stream));
 }
 
+fp8sm_status fp8sm_rate_probe(int32_t widen, int32_t blocks, int32_t waves_per_block,
+                              int32_t iters, float* sink, hipStream_t stream) {
+  if (widen < 0 || widen > 1) return FP8SM_ERR_UNSUPPORTED;
+  if (waves_per_block != 4 && waves_per_block != 8 && waves_per_block != 16)
+    return FP8SM_ERR_UNSUPPORTED;
+  if (!sink) return FP8SM_ERR_NULL;
+  if (!aligned(sink, 4)) return FP8SM_ERR_ALIGN;
+  if (blocks < 1 || iters < 1) return FP8SM_ERR_SHAPE;
+  if (blocks > 65536 || iters > (1 << 24)) return FP8SM_ERR_RANGE;
+  fp8sm_status st = check_device();
+  if (st != FP8SM_OK) return st;
+  return launched(launch_rate_probe(widen, blocks, waves_per_block, iters, sink, stream));
+}
+
 fp8sm_status fp8sm_scaled_mm_batched(int64_t nbatch, const int32_t* rows, const uint8_t* A,
                                      int64_t bs_a, int64_t lda, const uint8_t* B, int64_t bs_b,
                                      int64_t ldb, void* C, int64_t bs_c, int64_t ldc, int64_t M,

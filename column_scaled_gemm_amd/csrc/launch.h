@@ -118,6 +118,8 @@ hipError_t launch_gemm_rowwise_fp8mfma(const GemmArgs& g, hipStream_t s);
 // One matrix instruction on host-supplied register images (probe.hip).
 hipError_t launch_mfma_probe(int instr, const uint32_t* a, const uint32_t* b, float* d,
                              hipStream_t s);
+hipError_t launch_rate_probe(int widen, int blocks, int waves_per_block, int iters, float* sink,
+                             hipStream_t s);
 hipError_t launch_fill_k0(uint16_t* C, int64_t ldc, int64_t M, int64_t N, const void* bias,
                           hipStream_t s, const GemmBatch& bt = GemmBatch{1, 0, 0, 0, 0, 0, nullptr});
 

@@ -65,6 +65,58 @@ __global__ __launch_bounds__(64) void mfma_probe_kernel(int instr, const uint32_
   for (int v = 0; v < 16; ++v) d[l * 16 + v] = out[v];
 }
 
+// Matrix-pipe throughput ceiling (test hook behind fp8sm_rate_probe): every
+// wavefront runs `iters` iterations of four independent
+// v_mfma_f32_32x32x16_bf16 on register operands, the accumulator count and
+// instruction of the GEMMs' inner loop.  WIDEN: each iteration also widens
+// 16 fp8 dwords with v_cvt_scalef32_pk_bf16_fp8 (the GEMMs' ratio of widen
+// to matrix instructions for a 64 x 64 wavefront tile) and the widened values
+// are the next iteration's operands, so the widen sits on the matrix
+// instructions' critical path as it does in the GEMMs.  Nothing is read from
+// memory; each lane writes one float so no work is optimized away.
+template <bool WIDEN>
+__global__ __launch_bounds__(1024) void rate_probe_kernel(int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = 0x3f803f80u + (uint32_t)lane;
+  u32x4 ra = {base, base ^ 1u, base ^ 2u, base ^ 3u}, rb = {base ^ 4u, base ^ 5u, base ^ 6u, base ^ 7u};
+  uint32_t u[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) u[j] = 0x38383838u + (uint32_t)(lane * 16 + j);
+  f32x16p acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, ra), y = __builtin_bit_cast(bf16x8, rb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, acc[j], 0, 0, 0);
+    if constexpr (WIDEN) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        u[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u[j], 1.0f, false));
+      ra = u32x4{u[0] ^ u[4], u[1] ^ u[5], u[2] ^ u[6], u[3] ^ u[7]};
+      rb = u32x4{u[8] ^ u[12], u[9] ^ u[13], u[10] ^ u[14], u[11] ^ u[15]};
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sum += acc[j][v];
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum + (float)(ra[0] & 1u);
+}
+
+hipError_t launch_rate_probe(int widen, int blocks, int waves_per_block, int iters, float* sink,
+                             hipStream_t s) {
+  const dim3 grid((unsigned)blocks), block((unsigned)(64 * waves_per_block));
+  if (widen)
+    hipLaunchKernelGGL(rate_probe_kernel<true>, grid, block, 0, s, iters, sink);
+  else
+    hipLaunchKernelGGL(rate_probe_kernel<false>, grid, block, 0, s, iters, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_mfma_probe(int instr, const uint32_t* a, const uint32_t* b, float* d,
                              hipStream_t s) {
   hipLaunchKernelGGL(mfma_probe_kernel, dim3(1), dim3(64), 0, s, instr, a, b, d);

@@ -57,6 +57,7 @@ SIGNATURES = {
     "fp8sm_scaled_mm_fp8mfma": (_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _int, _p,
                                        _int, _p, _p]),
     "fp8sm_mfma_probe": (_int, [_i32, _p, _p, _p, _p]),
+    "fp8sm_rate_probe": (_int, [_i32, _i32, _i32, _i32, _p, _p]),
 }
 
 _lib = None
@@ -324,6 +325,18 @@ def mfma_probe(instr, a_regs, b_regs, stream=None):
     st = _load().fp8sm_mfma_probe(instr, _ptr(a_regs), _ptr(b_regs), _ptr(d), _stream(stream))
     _check(st, "fp8sm_mfma_probe")
     return d
+
+
+def rate_probe(widen, blocks, waves_per_block, iters, stream=None):
+    """Test hook fp8sm_rate_probe: launches the matrix-pipe throughput kernel
+    on the current device and returns its sink tensor (the caller times the
+    launch; 2*32*32*16*4*iters flops per wavefront)."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    sink = torch.empty(blocks * 64 * waves_per_block, dtype=torch.float32, device=dev)
+    st = _load().fp8sm_rate_probe(widen, blocks, waves_per_block, iters, _ptr(sink),
+                                  _stream(stream))
+    _check(st, "fp8sm_rate_probe")
+    return sink
 
 
 # ---------------------------------------------------------------- batched calls

@@ -372,6 +372,27 @@ fp8sm_status fp8sm_scaled_mm_fp8mfma(const uint8_t* A, int64_t lda, const uint8_
 fp8sm_status fp8sm_mfma_probe(int32_t instr, const uint32_t* a_regs, const uint32_t* b_regs,
                               float* d_regs, hipStream_t stream);
 
+/*
+ * Test hook (evidence, not part of the path): the matrix pipe's throughput
+ * ceiling for the GEMMs' inner loop.  A grid of `blocks` workgroups of
+ * 64 * waves_per_block threads; every wavefront runs `iters` iterations of
+ * four independent v_mfma_f32_32x32x16_bf16 on register operands
+ * (2 * 32 * 32 * 16 * 4 flops per iteration), with widen = 1 also sixteen
+ * v_cvt_scalef32_pk_bf16_fp8 per iteration whose results are the next
+ * iteration's operands (the GEMMs' widen-to-matrix ratio for a 64 x 64
+ * wavefront tile; the operand values are then arbitrary bit patterns, NaN
+ * included, which the throughput does not depend on).  Reads no memory; the
+ * caller times the launch (the dense
+ * bf16 peak, [P1] Kernel results' compute-bound shapes, is the reference).
+ *   sink   device float [blocks * 64 * waves_per_block], 4-byte aligned:
+ *          one value per lane, written so no work is optimized away.
+ * Errors: widen not 0/1 or waves_per_block not 4, 8 or 16 -> ERR_UNSUPPORTED;
+ * NULL -> ERR_NULL; blocks or iters < 1 -> ERR_SHAPE; blocks > 65536 or
+ * iters > 2^24 -> ERR_RANGE.
+ */
+fp8sm_status fp8sm_rate_probe(int32_t widen, int32_t blocks, int32_t waves_per_block,
+                              int32_t iters, float* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -231,6 +231,21 @@ def test_scatter_quant_rejects_bad_arguments():
     assert sc(T=0) == E["OK"] and sc(topk=0) == E["OK"] and sc(R=0) == E["OK"]
 
 
+def test_rate_probe_rejects_bad_arguments_before_any_launch():
+    from column_scaled_gemm_amd import fp8sm
+    lib = fp8sm.lib()
+    E = {v: k for k, v in fp8sm.STATUS.items()}
+    P = ctypes.c_void_p
+
+    def rp(widen=0, blocks=4, wpb=4, iters=8, sink=16):
+        return lib.fp8sm_rate_probe(widen, blocks, wpb, iters, P(sink), P(0))
+    assert rp(widen=2) == E["ERR_UNSUPPORTED"] and rp(widen=-1) == E["ERR_UNSUPPORTED"]
+    assert rp(wpb=2) == E["ERR_UNSUPPORTED"] and rp(wpb=32) == E["ERR_UNSUPPORTED"]
+    assert rp(sink=0) == E["ERR_NULL"] and rp(sink=2) == E["ERR_ALIGN"]
+    assert rp(blocks=0) == E["ERR_SHAPE"] and rp(iters=0) == E["ERR_SHAPE"]
+    assert rp(blocks=65537) == E["ERR_RANGE"] and rp(iters=(1 << 24) + 1) == E["ERR_RANGE"]
+
+
 def test_variant_names_and_forcing():
     from column_scaled_gemm_amd import fp8sm
     assert fp8sm.variant_count() >= 3
