@@ -340,17 +340,15 @@ __global__ __launch_bounds__(1024) void quant_g128_fused_kernel(
   SiluTable<F16>::load(tab, threadIdx.x, 1024);
   __syncthreads();
   const int64_t step = 16 * nw;
-  // Two steps per iteration with one exit test: both halves always run (a
-  // step past the end loads clamped rows and stores nothing), so the loop
-  // has no early exit whose join would make the compiler drain every load in
-  // flight at the loop head.
-  for (; g0 < total; g0 += 2 * step) {
+  while (g0 < total) {
+    g0 += step;
     fetch(b);
     convert(a);
+    if (g0 >= total) break;
+    g0 += step;
     fetch(a);
     convert(b);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last, unused prefetch
 }
 
 // ---------------------------------------------------------------------------
