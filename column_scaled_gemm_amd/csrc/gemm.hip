@@ -808,15 +808,17 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel (M <= 32 * TMD): a workgroup of NWD wavefronts owns 32 output
-// columns.  Wavefront w computes the canonical blocks w, w + NWD, ... of K,
+// Decode kernel (M <= 32 * TMD): a workgroup of NWD wavefronts owns PW output
+// columns (32, or 16 for twice the workgroups: the 32-row B operand then
+// repeats rows 0..15 in lanes 16..31 from the same LDS bytes, and output
+// columns 16..31 of the instruction are not stored).  Wavefront w computes the canonical blocks w, w + NWD, ... of K,
 // each a fresh partial chained through its chunks; after each round of NWD
 // blocks the partials meet in LDS and wavefront 0 adds them to its master in
 // ascending block order: the same fp32 operations in the same order as the
 // tile kernels, so every row is bitwise identical to theirs, while the
 // wavefronts' chains run side by side.
 //
-// The weight block (32 rows x 512 bytes) is what streams from HBM.  It is
+// The weight block (PW rows x 512 bytes) is what streams from HBM.  It is
 // copied by global->LDS DMA into the wavefront's own LDS region, each copy
 // instruction taking two whole 512-byte rows (every cache line it touches is
 // used whole), and read back in the matrix layout; no other wavefront reads
@@ -836,7 +838,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 // addresses (pieces past K re-read the row's last 16 bytes) and multiplied
 // with its A values past K -- and all of them outside the block that owns
 // that chunk -- zeroed.
-template <int TMD, int NWD, bool PART, int EPI>
+template <int TMD, int NWD, int PW, bool PART, int EPI>
 __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
@@ -844,9 +846,10 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
     GemmBatch gb) {
   constexpr int D = kBlockChunks;
   constexpr int RB = D * kChunk;   // bytes of a block row (512)
-  constexpr int REG = 32 * RB;     // a wavefront's LDS region: 32 rows of a block
+  constexpr int REG = PW * RB;     // a wavefront's LDS region: PW rows of a block
   constexpr int NCP = REG / 1024;  // copy instructions per block (two rows each)
   static_assert(RB == 512, "two block rows per 64-lane copy of 16 bytes each");
+  static_assert(PW == 16 || PW == 32, "panel width");
   __shared__ __attribute__((aligned(1024))) uint8_t bls[NWD * REG];
   __shared__ f32x16 part[NWD][TMD][64];
   {
@@ -862,7 +865,7 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, r32 = lane & 31;
-  const int n0 = blockIdx.x * 32;
+  const int n0 = blockIdx.x * PW;
   const int nf = K / kChunk;  // whole chunks
   const int nkc = (K + kChunk - 1) / kChunk;
   const int nblk = (nkc + D - 1) / D;
@@ -886,12 +889,13 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
     }
   };
   // fragment reads: row r32 of the region, logical pieces 4d + 2h + q
-  const uint8_t* myrow = bls + w * REG + r32 * RB;
+  const int prow = r32 % PW;  // PW = 16: lanes 16..31 repeat rows 0..15
+  const uint8_t* myrow = bls + w * REG + prow * RB;
   auto read_b = [&](Frag32 (&rb)[D]) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      rb[d].q[0] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h) ^ (r32 & 15)));
-      rb[d].q[1] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h + 1) ^ (r32 & 15)));
+      rb[d].q[0] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h) ^ (prow & 15)));
+      rb[d].q[1] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h + 1) ^ (prow & 15)));
     }
   };
 
@@ -923,7 +927,7 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
   // the chunk past the whole chunks, at clamped offsets
   const int kpart = nf * kChunk + 32 * h;
   const int poff0 = min(kpart, K - 16), poff1 = min(kpart + 16, K - 16);
-  const uint32_t brow = (uint32_t)(min(r32, last) * ldb);
+  const uint32_t brow = (uint32_t)(min(prow, last) * ldb);
 
   f32x16 mast[TMD][1], acc[TMD][1];
 #pragma unroll
@@ -999,7 +1003,7 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
     if (rr >= M) continue;
     const float sar = sa[sa_vec ? rr : 0];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < PW / 8; ++v) {
       const int c = n0 + 8 * v + 4 * h;
       if (c >= N) continue;
       const f32x4 a4 = {mast[i][0][4 * v], mast[i][0][4 * v + 1], mast[i][0][4 * v + 2],
@@ -1159,6 +1163,7 @@ const char* variant_name(int v) {
     case VAR_DECODE_32: return "decode32";
     case VAR_DECODE_64: return "decode64";
     case VAR_DECODE_32_W4: return "decode32w4";
+    case VAR_DECODE_16: return "decode16";
     default: return "unknown";
   }
 }
@@ -1169,7 +1174,8 @@ bool variant_accepts(int v, int64_t M) {
     case VAR_TILE_128x256:
     case VAR_TILE_256x128: return true;
     case VAR_DECODE_32:
-    case VAR_DECODE_32_W4: return M <= 32;
+    case VAR_DECODE_32_W4:
+    case VAR_DECODE_16: return M <= 32;
     case VAR_DECODE_64: return M <= 64;
     default: return false;
   }
@@ -1205,14 +1211,14 @@ static hipError_t launch_rowwise_tile(const GemmArgs& g, hipStream_t s) {
   });
 }
 
-template <int TMD, int NWD>
+template <int TMD, int NWD, int PW = 32>
 static hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
-  const int grid = (int)((g.N + 31) / 32);
+  const int grid = (int)((g.N + PW - 1) / PW);
   auto go = [&](auto part) {
     return with_epi(g, [&](auto e) {
       constexpr int EPI = decltype(e)::value;
       constexpr bool PART = decltype(part)::value;
-      hipLaunchKernelGGL((gemm_decode_kernel<TMD, NWD, PART, EPI>), grid2(grid, g),
+      hipLaunchKernelGGL((gemm_decode_kernel<TMD, NWD, PW, PART, EPI>), grid2(grid, g),
                          dim3(64 * NWD), 0, s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M,
                          (int)g.N, (int)g.K, static_cast<const float*>(g.sa),
                          (int)(g.sa_kind == 1), static_cast<const float*>(g.sb),
@@ -1230,6 +1236,7 @@ hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
     case VAR_DECODE_32: return launch_decode<1, 8>(g, s);
     case VAR_DECODE_64: return launch_decode<2, 4>(g, s);
     case VAR_DECODE_32_W4: return launch_decode<1, 4>(g, s);
+    case VAR_DECODE_16: return launch_decode<1, 8, 16>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

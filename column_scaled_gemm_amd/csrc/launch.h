@@ -107,7 +107,8 @@ enum Variant {
   VAR_DECODE_32 = 3,     // M <= 32: eight wavefronts per 32 columns, one 512-K block each
   VAR_DECODE_64 = 4,     // M <= 64: four wavefronts per 32 columns
   VAR_DECODE_32_W4 = 5,  // M <= 32: four wavefronts per 32 columns, two workgroups per CU
-  VAR_COUNT = 6
+  VAR_DECODE_16 = 6,     // M <= 32: eight wavefronts per 16 columns (twice the workgroups)
+  VAR_COUNT = 7
 };
 const char* variant_name(int v);
 bool variant_accepts(int v, int64_t M);

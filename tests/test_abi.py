@@ -262,7 +262,7 @@ def test_variant_names_and_forcing():
 def test_variant_accepts_bounds_decode_variants_by_m():
     from column_scaled_gemm_amd import fp8sm
     names = {fp8sm.variant_name(v): v for v in range(fp8sm.variant_count())}
-    for name, cap in (("decode32", 32), ("decode32w4", 32), ("decode64", 64)):
+    for name, cap in (("decode32", 32), ("decode32w4", 32), ("decode16", 32), ("decode64", 64)):
         v = names[name]
         assert fp8sm.variant_accepts(v, cap, 4096, 65536)
         assert not fp8sm.variant_accepts(v, cap + 1, 4096, 4096)
