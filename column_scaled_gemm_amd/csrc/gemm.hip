@@ -212,6 +212,23 @@ __device__ __forceinline__ void store_row4(uint16_t* __restrict__ C, int64_t ldc
   *reinterpret_cast<uint2*>(C + (int64_t)r * ldc + c) = make_uint2(lo, hi);
 }
 
+// The same for two consecutive outputs (columns c, c + 1, c even): one 4-byte
+// store.
+template <int EPI>
+__device__ __forceinline__ void store_row2(uint16_t* __restrict__ C, int64_t ldc, int r, int c,
+                                           float a0, float a1, float sar,
+                                           const float* __restrict__ sb, int sb_vec,
+                                           const uint16_t* __restrict__ bias) {
+  const float y0 = epi_value<EPI>(a0, sar, sb[sb_vec ? c : 0], bias, c);
+  const float y1 = epi_value<EPI>(a1, sar, sb[sb_vec ? c + 1 : 0], bias, c + 1);
+  uint32_t v;
+  if constexpr ((EPI & EPI_F16) != 0)
+    v = (uint32_t)epi_round<EPI>(y0) | ((uint32_t)epi_round<EPI>(y1) << 16);
+  else
+    v = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)y0, (__bf16)y1});
+  *reinterpret_cast<uint32_t*>(C + (int64_t)r * ldc + c) = v;
+}
+
 // Hardware places consecutive workgroups on the 8 XCDs in turn; give each XCD
 // a contiguous range of logical tiles (so tiles sharing A / B panels share an
 // L2), then walk the logical tiles in groups of kGroupM tile rows.
@@ -811,12 +828,14 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 // Decode kernel (M <= 32 * TMD): a workgroup of NWD wavefronts owns PW output
 // columns (32, or 16 for twice the workgroups: the 32-row B operand then
 // repeats rows 0..15 in lanes 16..31 from the same LDS bytes, and output
-// columns 16..31 of the instruction are not stored).  Wavefront w computes the canonical blocks w, w + NWD, ... of K,
-// each a fresh partial chained through its chunks; after each round of NWD
-// blocks the partials meet in LDS and wavefront 0 adds them to its master in
-// ascending block order: the same fp32 operations in the same order as the
-// tile kernels, so every row is bitwise identical to theirs, while the
-// wavefronts' chains run side by side.
+// columns 16..31 of the instruction are not stored).  Wavefront w computes
+// the canonical blocks w, w + NWD, ... of K, each a fresh partial chained
+// through its chunks; after each round of NWD blocks the partials meet in
+// LDS and every wavefront adds its slice (16 / NWD of each lane's 16
+// accumulator elements) of every partial to its master, in ascending block
+// order, and finally stores that slice: the same fp32 operations in the same
+// order as the tile kernels, so every row is bitwise identical to theirs,
+// while the wavefronts' chains, reductions and stores run side by side.
 //
 // The weight block (PW rows x 512 bytes) is what streams from HBM.  It is
 // copied by global->LDS DMA into the wavefront's own LDS region, each copy
@@ -851,7 +870,9 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
   static_assert(RB == 512, "two block rows per 64-lane copy of 16 bytes each");
   static_assert(PW == 16 || PW == 32, "panel width");
   __shared__ __attribute__((aligned(1024))) uint8_t bls[NWD * REG];
-  __shared__ f32x16 part[NWD][TMD][64];
+  __shared__ float part[NWD][TMD][16][64];  // element-major: conflict-free slices
+  constexpr int EPW = 16 / NWD;              // accumulator elements each wavefront reduces
+  static_assert(EPW * NWD == 16 && 4 % EPW == 0, "slices of the 16 accumulator elements");
   {
     const int64_t bi = blockIdx.y;
     A += bi * gb.a;
@@ -929,11 +950,13 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
   const int poff0 = min(kpart, K - 16), poff1 = min(kpart + 16, K - 16);
   const uint32_t brow = (uint32_t)(min(prow, last) * ldb);
 
-  f32x16 mast[TMD][1], acc[TMD][1];
+  // wavefront w keeps the master of accumulator elements w*EPW .. w*EPW+EPW-1
+  float mast[TMD][EPW];
+  f32x16 acc[TMD][1];
 #pragma unroll
   for (int i = 0; i < TMD; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mast[i][0][v] = 0.f;
+    for (int e = 0; e < EPW; ++e) mast[i][e] = 0.f;
   Frag32 rb[D], ra[D][TMD];
   if (nf > 0) {
     issue_block(min(w, nblk - 1));
@@ -982,33 +1005,33 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
       mma32_chunk<TMD, 1, false>(pa, one, pb, acc);
     }
 #pragma unroll
-    for (int i = 0; i < TMD; ++i) part[w][i][lane] = acc[i][0];
+    for (int i = 0; i < TMD; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) part[w][i][e][lane] = acc[i][0][e];
     __syncthreads();
-    if (w == 0) {
-      for (int b = 0; b < NWD && r + b < nblk; ++b)
+    // every wavefront adds its slice of each block's partial, blocks ascending
+    for (int b = 0; b < NWD && r + b < nblk; ++b)
 #pragma unroll
-        for (int i = 0; i < TMD; ++i) {
-          const f32x16 p = part[b][i][lane];
+      for (int i = 0; i < TMD; ++i)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) mast[i][0][v] = mast[i][0][v] + p[v];
-        }
-    }
+        for (int e = 0; e < EPW; ++e) mast[i][e] = mast[i][e] + part[b][i][w * EPW + e][lane];
     __syncthreads();
   }
-  if (w != 0) return;
-  // lane l holds output row 32i + l % 32 and the columns 8v + 4(l / 32) .. +3
+  // accumulator element e of lane l is output row 32i + l % 32, column
+  // 8 (e / 4) + 4 (l / 32) + e % 4; wavefront w stores its elements
+  const int v = (w * EPW) / 4, t0 = (w * EPW) % 4;
+  if (v >= PW / 8) return;  // PW = 16: the instruction's upper 16 columns
 #pragma unroll
   for (int i = 0; i < TMD; ++i) {
     const int rr = 32 * i + r32;
-    if (rr >= M) continue;
+    const int c = n0 + 8 * v + 4 * h + t0;
+    if (rr >= M || c >= N) continue;
     const float sar = sa[sa_vec ? rr : 0];
-#pragma unroll
-    for (int v = 0; v < PW / 8; ++v) {
-      const int c = n0 + 8 * v + 4 * h;
-      if (c >= N) continue;
-      const f32x4 a4 = {mast[i][0][4 * v], mast[i][0][4 * v + 1], mast[i][0][4 * v + 2],
-                        mast[i][0][4 * v + 3]};
+    if constexpr (EPW == 4) {
+      const f32x4 a4 = {mast[i][0], mast[i][1], mast[i][2], mast[i][3]};
       store_row4<EPI>(C, ldc, rr, c, a4, sar, sb, sb_vec, bias);
+    } else {
+      store_row2<EPI>(C, ldc, rr, c, mast[i][0], mast[i][1], sar, sb, sb_vec, bias);
     }
   }
 }
