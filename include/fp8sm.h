@@ -332,7 +332,7 @@ int fp8sm_pick_variant(int64_t M, int64_t N, int64_t K);
 
 /* Test hook: 1 if variant `id` computes rowwise/per-tensor calls of this
  * shape, else 0 (a forced variant that does not is ERR_UNSUPPORTED).  The
- * decode variants bound M (16 / 32 / 64); the tile variants take any shape
+ * decode variants bound M (32 or 64); the tile variants take any shape
  * the call accepts. */
 int fp8sm_variant_accepts(int id, int64_t M, int64_t N, int64_t K);
 
