@@ -838,16 +838,16 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 // while the wavefronts' chains, reductions and stores run side by side.
 //
 // The weight block (PW rows x 512 bytes) is what streams from HBM.  It is
-// copied by global->LDS DMA into the wavefront's own LDS region, each copy
-// instruction taking two whole 512-byte rows (every cache line it touches is
-// used whole), and read back in the matrix layout; no other wavefront reads
-// the region, so waiting for the wavefront's own copies is enough (no
-// barrier).  Within a row, 16-byte piece p sits at position p ^ (row % 16),
-// so each 16-lane phase of a fragment read hits 16 distinct bank groups.  The
-// copies of a wavefront's next block are issued as soon as the current
-// block's fragments are in registers, so they overlap its chain.  The few A
-// rows (L2-resident, shared by every workgroup) are read straight into
-// registers.
+// copied by global->LDS DMA into the wavefront's own LDS region, pair of
+// chunks by pair of chunks (each copy instruction takes 8 rows x 128 bytes:
+// whole cache lines), and read back in the matrix layout through a bank
+// swizzle; no other wavefront reads the region, so waiting for the
+// wavefront's own copies is enough (no barrier).  With one round of blocks
+// the matrix steps of each chunk pair start as soon as its copies have
+// landed; with several, the copies of a wavefront's next block are issued as
+// soon as the current block's fragments are in registers, so they overlap
+// its chain.  The few A rows (L2-resident, shared by every workgroup) are
+// read straight into registers.
 //
 // A chunk slot past the wavefront's whole chunks (its block is the last one
 // and partial, or it has no block this round) is multiplied with its A
@@ -857,7 +857,17 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
 // addresses (pieces past K re-read the row's last 16 bytes) and multiplied
 // with its A values past K -- and all of them outside the block that owns
 // that chunk -- zeroed.
-template <int TMD, int NWD, int PW, bool PART, int EPI>
+// f(std::integral_constant<int, i>) for i = 0 .. N - 1 (compile-time indices,
+// e.g. for wait counts that must be immediates).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+template <int TMD, int NWD, int PW, bool PART, bool REFILL, int EPI>
 __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
@@ -892,32 +902,63 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
   const int nblk = (nkc + D - 1) / D;
   const int last = N - 1 - n0;  // B rows past N repeat the last row
 
-  // copy instruction j fills rows 2j, 2j + 1 of the region: lane l copies
-  // row 2j + l / 32, logical piece (l % 32) ^ (row % 16) into position l % 32.
-  // Row offsets stay below 2^31 (32 rows of at most 2^24 bytes, plus K).
+  // One round: the region is pair-major: chunk pair p of the block holds PW
+  // rows x 128 bytes (chunks 2p, 2p + 1 of each row: one whole cache line),
+  // the 16-byte pieces of row r XOR-swizzled by (r / 2) % 8 so a 16-lane read
+  // of 16 rows hits 16 distinct bank groups.  Copy g of pair p fills rows
+  // 8g .. 8g + 7: lane l copies row 8g + l / 8, logical piece
+  // (l % 8) ^ ((row / 2) % 8) into position l % 8.  Row offsets stay below
+  // 2^31 (32 rows of at most 2^24 bytes, plus K).
+  constexpr int NP = D / 2;          // chunk pairs per block
+  constexpr int NGP = PW / 8;        // copies per pair
+  constexpr int PB = PW * 2 * kChunk;  // region bytes per pair
   const uint8_t* bbase = B + (int64_t)n0 * ldb;
   const i32x4 rsb = sgpr_rsrc(bbase);
   const uint32_t region =
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)bls) + (uint32_t)(w * REG);
+  // Several rounds (REFILL) stream better with the row-major layout: copy j
+  // takes rows 2j, 2j + 1 whole (lane l: row 2j + l / 32, logical piece
+  // (l % 32) ^ (row % 16) into position l % 32).
+  const int crow = lane >> 3;
   auto issue_block = [&](int blk) {
     const int kwhole = nf * kChunk;
+    if constexpr (REFILL) {
 #pragma unroll
-    for (int j = 0; j < NCP; ++j) {
-      const int row = min(2 * j + h, last);
-      const int kp = blk * RB + 16 * (r32 ^ (row & 15));
-      const uint32_t off = (uint32_t)(row * ldb) + (uint32_t)(kp + 16 <= kwhole ? kp : 0);
-      dma16_buf(off, rsb, 0, region + (uint32_t)(j * 1024));
+      for (int j = 0; j < NCP; ++j) {
+        const int row = min(2 * j + h, last);
+        const int kp = blk * RB + 16 * (r32 ^ (row & 15));
+        const uint32_t off = (uint32_t)(row * ldb) + (uint32_t)(kp + 16 <= kwhole ? kp : 0);
+        dma16_buf(off, rsb, 0, region + (uint32_t)(j * 1024));
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int g = 0; g < NGP; ++g) {
+          const int rl = 8 * g + crow;
+          const int row = min(rl, last);
+          const int kp = blk * RB + p * 2 * kChunk + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
+          const uint32_t off = (uint32_t)(row * ldb) + (uint32_t)(kp + 16 <= kwhole ? kp : 0);
+          dma16_buf(off, rsb, 0, region + (uint32_t)(p * PB + g * 1024));
+        }
     }
   };
-  // fragment reads: row r32 of the region, logical pieces 4d + 2h + q
+  // fragment read of chunk d: logical pieces 4d + 2h + q of row prow (row-major
+  // layout) or 4 (d % 2) + 2h + q of row prow in pair d / 2 (pair-major)
   const int prow = r32 % PW;  // PW = 16: lanes 16..31 repeat rows 0..15
-  const uint8_t* myrow = bls + w * REG + prow * RB;
-  auto read_b = [&](Frag32 (&rb)[D]) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      rb[d].q[0] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h) ^ (prow & 15)));
-      rb[d].q[1] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h + 1) ^ (prow & 15)));
+  const uint8_t* myrow = bls + w * REG + prow * (REFILL ? RB : 2 * kChunk);
+  const int rsw = REFILL ? (prow & 15) : ((prow >> 1) & 7);
+  auto read_chunk = [&](int d) -> Frag32 {
+    Frag32 f;
+    if constexpr (REFILL) {
+      f.q[0] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h) ^ rsw));
+      f.q[1] = *reinterpret_cast<const uint4*>(myrow + 16 * ((4 * d + 2 * h + 1) ^ rsw));
+    } else {
+      const uint8_t* pr = myrow + (d >> 1) * PB;
+      f.q[0] = *reinterpret_cast<const uint4*>(pr + 16 * ((4 * (d & 1) + 2 * h) ^ rsw));
+      f.q[1] = *reinterpret_cast<const uint4*>(pr + 16 * ((4 * (d & 1) + 2 * h + 1) ^ rsw));
     }
+    return f;
   };
 
   uint32_t arow[TMD];
@@ -957,10 +998,22 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
   for (int i = 0; i < TMD; ++i)
 #pragma unroll
     for (int e = 0; e < EPW; ++e) mast[i][e] = 0.f;
-  Frag32 rb[D], ra[D][TMD];
+  Frag32 ra[D][TMD];
+  // One round (REFILL false): A loads first, then the copies pair by pair, so
+  // a wait for pair p's copies (at most (NP - 1 - p) NGP copies outstanding)
+  // also covers every A load and each pair's matrix steps start as soon as
+  // its copies have landed.  Several rounds (REFILL): the weight copies go
+  // out first (they are the long pole), the next round's copies are issued
+  // as soon as this round's fragments are in registers, and its A loads
+  // after the chain.
   if (nf > 0) {
-    issue_block(min(w, nblk - 1));
-    load_a(min(w, nblk - 1), ra);
+    if constexpr (REFILL) {
+      issue_block(min(w, nblk - 1));
+      load_a(min(w, nblk - 1), ra);
+    } else {
+      load_a(min(w, nblk - 1), ra);
+      issue_block(min(w, nblk - 1));
+    }
   }
   for (int r = 0; r < nblk; r += NWD) {
     const int blk = r + w;
@@ -969,15 +1022,8 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][0][v] = 0.f;
     if (nf > 0) {
-      wait_vmcnt<0>();  // this round's copies and A loads
-      read_b(rb);
       const int nwhole = max(0, min(D, nf - blk * D));  // 0 when blk >= nblk
-      if (r + NWD < nblk) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region has been read
-        issue_block(min(blk + NWD, nblk - 1));
-      }
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
+      auto chunk_mma = [&](int d, const Frag32& fbd) {
         const bool own = d < nwhole;
         Frag32 fa[TMD];
 #pragma unroll
@@ -985,10 +1031,31 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
           fa[i].q[0] = own ? ra[d][i].q[0] : z4;
           fa[i].q[1] = own ? ra[d][i].q[1] : z4;
         }
-        const Frag32 fb[1] = {rb[d]};
+        const Frag32 fb[1] = {fbd};
         mma32_chunk<TMD, 1, false>(fa, one, fb, acc);
+      };
+      if constexpr (!REFILL) {
+        static_for<NP>([&](auto pc) {
+          constexpr int p = decltype(pc)::value;
+          wait_vmcnt<(NP - 1 - p) * NGP>();
+          const Frag32 f0 = read_chunk(2 * p), f1 = read_chunk(2 * p + 1);
+          chunk_mma(2 * p, f0);
+          chunk_mma(2 * p + 1, f1);
+        });
+      } else {
+        wait_vmcnt<0>();  // this round's copies and A loads
+        Frag32 rb[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) rb[d] = read_chunk(d);
+        const bool next = r + NWD < nblk;  // uniform
+        if (next) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region has been read
+          issue_block(blk + NWD < nblk ? blk + NWD : nblk - 1);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) chunk_mma(d, rb[d]);
+        if (next) load_a(min(blk + NWD, nblk - 1), ra);
       }
-      if (r + NWD < nblk) load_a(min(blk + NWD, nblk - 1), ra);
     }
     if constexpr (PART) {
       const bool own = blk == nf / D;
@@ -1237,18 +1304,26 @@ static hipError_t launch_rowwise_tile(const GemmArgs& g, hipStream_t s) {
 template <int TMD, int NWD, int PW = 32>
 static hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
   const int grid = (int)((g.N + PW - 1) / PW);
-  auto go = [&](auto part) {
+  auto go = [&](auto part, auto refill) {
     return with_epi(g, [&](auto e) {
       constexpr int EPI = decltype(e)::value;
-      constexpr bool PART = decltype(part)::value;
-      hipLaunchKernelGGL((gemm_decode_kernel<TMD, NWD, PW, PART, EPI>), grid2(grid, g),
+      constexpr bool PART = decltype(part)::value, REFILL = decltype(refill)::value;
+      hipLaunchKernelGGL((gemm_decode_kernel<TMD, NWD, PW, PART, REFILL, EPI>), grid2(grid, g),
                          dim3(64 * NWD), 0, s, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M,
                          (int)g.N, (int)g.K, static_cast<const float*>(g.sa),
                          (int)(g.sa_kind == 1), static_cast<const float*>(g.sb),
                          (int)(g.sb_kind == 2), static_cast<const uint16_t*>(g.bias), g.batch);
     });
   };
-  return g.K % kChunk ? go(std::true_type{}) : go(std::false_type{});
+  // REFILL: K has more blocks than the workgroup has wavefronts, so the
+  // kernel runs several rounds with each next block's copies issued ahead;
+  // otherwise one round whose chunk pairs are multiplied as they land
+  const int64_t nblk = (g.K + kChunk * kBlockChunks - 1) / (kChunk * kBlockChunks);
+  if (nblk > NWD)
+    return g.K % kChunk ? go(std::true_type{}, std::true_type{})
+                        : go(std::false_type{}, std::true_type{});
+  return g.K % kChunk ? go(std::true_type{}, std::false_type{})
+                      : go(std::false_type{}, std::false_type{});
 }
 
 hipError_t launch_gemm_rowwise(int variant, const GemmArgs& g, hipStream_t s) {
