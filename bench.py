@@ -102,7 +102,9 @@ def ceilings(repeats=5):
     and 4 wavefronts per SIMD, without and with the widen feeding the
     operands) and HBM (a 1 GiB copy and a 1 GiB read, caches evicted first
     by the other buffer).  Each figure is the median over `repeats` launches
-    timed with HIP events."""
+    timed with HIP events.  Last, the QKV GEMM on three data sets of the same
+    shape (the quantized workload, all-zero codes, all codes 1.0): the
+    difference is what the values themselves cost."""
     import numpy as np
     import torch
     from column_scaled_gemm_amd import fp8sm
@@ -168,6 +170,35 @@ def ceilings(repeats=5):
         gbs = nbytes / us / 1e3
         print(json.dumps({"ceiling": name, "us": round(us, 1), "GBps": round(gbs, 1),
                           "frac_of_hbm_peak": round(gbs / PEAK_HBM, 4)}), flush=True)
+    del src, dst, other
+
+    # Data-dependent cost of the rowwise GEMM: the QKV GEMM the dispatch picks,
+    # on the quantized workload, on all-zero codes and on codes that all
+    # encode 1.0 (0x38), interleaved over three rounds (median of each).  The
+    # kernel's instructions, addresses and memory traffic are the same in all
+    # three; only the values (and so the switching activity) differ.
+    from column_scaled_gemm_amd import inputs
+    M, N, K = inputs.ROWWISE_SHAPES["qkv"]
+    w = inputs.workload("qkv")
+    qb, sb = fp8sm.quant_group(w.w.to(dev), -1)
+    qa, sa = fp8sm.quant_group(w.x.to(dev), -1)
+    del w
+    sa, sb = sa.reshape(-1), sb.reshape(-1)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    data = {"quantized workload": (qa, qb),
+            "all-zero codes": (torch.zeros_like(qa), torch.zeros_like(qb)),
+            "all codes 0x38 (1.0)": (torch.full_like(qa, 0x38), torch.full_like(qb, 0x38))}
+    per = {k: [] for k in data}
+    for _ in range(3):
+        for k, (a, b) in data.items():
+            per[k].append(timed(lambda: fp8sm.scaled_mm(a, b, sa, sb, fp8sm.KIND_ROW,
+                                                        fp8sm.KIND_COL, c=c)))
+    variant = fp8sm.variant_name(fp8sm.pick_variant(M, N, K))
+    for k, xs in per.items():
+        us = float(np.median(xs))
+        print(json.dumps({"probe": "QKV rowwise GEMM %dx%dx%d, %s" % (M, N, K, k),
+                          "variant": variant, "us": round(us, 1),
+                          "TFLOPs": round(2.0 * M * N * K / us / 1e6, 1)}), flush=True)
 
 
 def cpu_baseline(w, M, N, K, target_s):

@@ -47,11 +47,14 @@ __device__ __forceinline__ void widen8(const uint4 v, float* f) {
 
 // Clamp to the E4M3FN range and convert eight fp32 values to codes
 // (round to nearest even, sign of zero kept).  The hardware conversion does
-// not saturate, so the clamp comes first.
+// not saturate, so the clamp comes first -- unless the caller knows every
+// value already lies in [-448, 448] (CLAMP false: a power-of-two multiplier
+// 2^-e with 448 * 2^e >= the group's absmax, which scales exactly).
+template <bool CLAMP = true>
 __device__ __forceinline__ uint2 to_e4m3_x8(const float* v) {
   float c[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(v[i], -kQMax), kQMax);
+  for (int i = 0; i < 8; ++i) c[i] = CLAMP ? fminf(fmaxf(v[i], -kQMax), kQMax) : v[i];
   int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
@@ -59,36 +62,35 @@ __device__ __forceinline__ uint2 to_e4m3_x8(const float* v) {
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
-// ceil(log2 s) for a positive normal fp32 s, from its bit fields.
-__device__ __forceinline__ int ue8m0_exponent(float s) {
-  const uint32_t b = __float_as_uint(s);
-  return (int)((b >> 23) & 0xFFu) - 127 + ((b & 0x7FFFFFu) != 0u ? 1 : 0);
-}
 __device__ __forceinline__ float pow2f(int e) {  // 2^e, -126 <= e <= 127
   return __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
 // v from lane (l + N) mod 16 of the same 16-lane DPP row.
 template <int N>
-__device__ __forceinline__ float dpp_row_ror(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_row_ror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xF, 0xF, false);
 }
 
-// Maximum over aligned groups of WIDTH lanes (16 or 64), returned in every
-// lane of the group.  Within a 16-lane row: four DPP rotations; across the
-// rows of a wavefront: two lane shuffles.
+// Maximum of non-negative fp32 values (absolute values: +0 and up, +inf
+// included) over aligned groups of WIDTH lanes (16 or 64), returned in every
+// lane of the group.  Such values order like their bit patterns, so the
+// maximum is taken on the patterns as unsigned integers: within a 16-lane row
+// four DPP rotations, each folded into the max instruction; across the rows
+// of a wavefront two lane shuffles.
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v) {
   static_assert(WIDTH == 16 || WIDTH == 64, "group width");
-  v = fmaxf(v, dpp_row_ror<8>(v));
-  v = fmaxf(v, dpp_row_ror<4>(v));
-  v = fmaxf(v, dpp_row_ror<2>(v));
-  v = fmaxf(v, dpp_row_ror<1>(v));
+  uint32_t b = __float_as_uint(v);
+  b = max(b, dpp_row_ror<8>(b));
+  b = max(b, dpp_row_ror<4>(b));
+  b = max(b, dpp_row_ror<2>(b));
+  b = max(b, dpp_row_ror<1>(b));
   if constexpr (WIDTH == 64) {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    b = max(b, (uint32_t)__shfl_xor((int)b, 16, 64));
+    b = max(b, (uint32_t)__shfl_xor((int)b, 32, 64));
   }
-  return v;
+  return __uint_as_float(b);
 }
 
 // Live rows of this workgroup's batch (blockIdx.y): clamp(rows[b], 0, M), or

@@ -32,18 +32,32 @@ constexpr int64_t kMaxRowBlocks = 1 << 20;
 template <int FMT>
 __device__ __forceinline__ float group_multiplier(float amax, float* scale_val, int* ebyte) {
   const float a = fmaxf(amax, kAmaxFloor);
-  const float s = a / kQMax;
   if constexpr (FMT == FMT_FP32) {
-    *scale_val = s;
+    *scale_val = a / kQMax;
     *ebyte = 0;
     return kQMax / a;
   } else {
-    const int e = ue8m0_exponent(s);
+    // e = ceil(log2 RN32(a / 448)) without the divide.  a is a normal fp32
+    // value (a >= 1e-10), a = (1 + m 2^-23) 2^(E-127).  RN32(a/448) <= 2^k
+    // exactly when a <= 448 * 2^k = 1.75 * 2^(k+8): if a is at most that,
+    // so is a/448 and its rounding; if a is larger it is at least one ulp
+    // (2^(k-15)) larger, so a/448 exceeds 2^k by more than 2^(k-24), half an
+    // ulp of 2^k, and rounds above it.  Hence e = E - 135 when m <= 0x600000
+    // (1 + m 2^-23 <= 1.75) and E - 134 otherwise: adding 0x1FFFFF carries
+    // into the exponent field exactly when m > 0x600000.
+    const uint32_t t = (__float_as_uint(a) + 0x1FFFFFu) & 0xFF800000u;  // E' << 23
+    const int e = (int)(t >> 23) - 135;
     *scale_val = pow2f(e);
     *ebyte = e + 127;
     return pow2f(-e);
   }
 }
+
+// Codes need the clamp to [-448, 448] only with fp32 scales: a UE8M0
+// multiplier 2^-e has 448 * 2^e >= the group's absmax (above), and scaling by
+// a power of two is exact, so every scaled value already lies in range.
+template <int FMT>
+constexpr bool kClampCodes = FMT == FMT_FP32;
 
 template <int FMT>
 __device__ __forceinline__ void store_scale(void* scales, int64_t idx, float v, int ebyte) {
@@ -107,7 +121,7 @@ __device__ __forceinline__ uint2 group128_codes(float* y, float* sval, int* eb) 
   const float mult = group_multiplier<FMT>(amax, sval, eb);
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = y[i] * mult;
-  return to_e4m3_x8(y);
+  return to_e4m3_x8<kClampCodes<FMT>>(y);
 }
 
 // Quantize one 1x128 group and store its codes and scale (row < 0: nothing).
@@ -144,7 +158,7 @@ __device__ __forceinline__ void quant_group128_o32(float* y, int l16, bool valid
   if (valid) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = y[i] * mult;
-    store_stream8(q + qo, to_e4m3_x8(y));
+    store_stream8(q + qo, to_e4m3_x8<kClampCodes<FMT>>(y));
     if (l16 == 0) store_scale<FMT>(scales, so, sval, eb);
   }
 }
@@ -413,7 +427,7 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
       widen8<F16>(v[i], y);
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
-      const uint2 codes = to_e4m3_x8(y);
+      const uint2 codes = to_e4m3_x8<kClampCodes<FMT>>(y);
       if (ok[i]) store_stream8(qr + (int64_t)cidx[i] * 8, codes);
     }
     if (lane == 0) store_scale<FMT>(scales, r, sval, eb);
@@ -490,7 +504,7 @@ __global__ __launch_bounds__(256) void quant_token_wg_kernel(
       widen8<F16>(v[i], y);
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
-      const uint2 codes = to_e4m3_x8(y);
+      const uint2 codes = to_e4m3_x8<kClampCodes<FMT>>(y);
       if (ok[i]) store_stream8(qr + (int64_t)cidx[i] * 8, codes);
     }
     if (threadIdx.x == 0) store_scale<FMT>(scales, r, sval, eb);
@@ -543,7 +557,7 @@ __device__ __forceinline__ void quant_row_2pass(const uint16_t* __restrict__ xr,
     load_values<F16, FUSED>(g, u, y, tab);
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = y[j] * mult;
-    *reinterpret_cast<uint2*>(qr + c * 8) = to_e4m3_x8(y);
+    *reinterpret_cast<uint2*>(qr + c * 8) = to_e4m3_x8<kClampCodes<FMT>>(y);
   }
   if (lane == 0) store_scale<FMT>(scales, row, sval, eb);
 }
