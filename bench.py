@@ -196,7 +196,7 @@ def ceilings(repeats=5):
     variant = fp8sm.variant_name(fp8sm.pick_variant(M, N, K))
     for k, xs in per.items():
         us = float(np.median(xs))
-        print(json.dumps({"probe": "QKV rowwise GEMM %dx%dx%d, %s" % (M, N, K, k),
+        print(json.dumps({"probe": "QKV rowwise GEMM %dx%dx%d, %s" % (M, K, N, k),
                           "variant": variant, "us": round(us, 1),
                           "TFLOPs": round(2.0 * M * N * K / us / 1e6, 1)}), flush=True)
 
