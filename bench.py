@@ -100,7 +100,7 @@ def ceilings(repeats=5):
     """Measured ceilings of the machine, one JSON line each: the matrix pipe
     on the GEMMs' instruction and accumulator count (fp8sm_rate_probe at 1, 2
     and 4 wavefronts per SIMD, without and with the widen feeding the
-    operands) and HBM (a 1 GiB copy and a 1 GiB read, caches evicted first
+    operands) and HBM (a 1 GiB copy, read and write, caches evicted first
     by the other buffer).  Each figure is the median over `repeats` launches
     timed with HIP events.  Last, the QKV GEMM on three data sets of the same
     shape (the quantized workload, all-zero codes, all codes 1.0): the
@@ -163,8 +163,19 @@ def ceilings(repeats=5):
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3
 
+    def write_cold():
+        torch.sum(other, dim=0, out=sink)   # evicts dst (1 GiB read)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.fill_(7)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3
+
     for name, fn, nbytes in (("HBM copy (torch copy_, 1 GiB read + 1 GiB write)", copy_cold, 2 * n),
-                             ("HBM read (torch sum, 1 GiB)", read_cold, n)):
+                             ("HBM read (torch sum, 1 GiB)", read_cold, n),
+                             ("HBM write (torch fill_, 1 GiB)", write_cold, n)):
         fn()
         us = float(np.median([fn() for _ in range(repeats)]))
         gbs = nbytes / us / 1e3
