@@ -381,9 +381,11 @@ fp8sm_status fp8sm_mfma_probe(int32_t instr, const uint32_t* a_regs, const uint3
  * v_cvt_scalef32_pk_bf16_fp8 per iteration whose results are the next
  * iteration's operands (the GEMMs' widen-to-matrix ratio for a 64 x 64
  * wavefront tile; the operand values are then arbitrary bit patterns, NaN
- * included, which the throughput does not depend on).  Reads no memory; the
- * caller times the launch (the dense
- * bf16 peak, [P1] Kernel results' compute-bound shapes, is the reference).
+ * included).  Reads no memory, so it measures issue rate near the rated
+ * clock, not the power-limited clock of real operands streaming from memory
+ * (the GEMMs on real data run measurably slower than on constant codes).
+ * The caller times the launch (the dense bf16 peak, [P1] Kernel results'
+ * compute-bound shapes, is the reference).
  *   sink   device float [blocks * 64 * waves_per_block], 4-byte aligned:
  *          one value per lane, written so no work is optimized away.
  * Errors: widen not 0/1 or waves_per_block not 4, 8 or 16 -> ERR_UNSUPPORTED;
