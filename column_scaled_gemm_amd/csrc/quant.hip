@@ -206,7 +206,10 @@ __global__ __launch_bounds__(256) void quant_g128_kernel(
 // scatter fusion): token t's groups are quantized once, as above, and each
 // group's codes and scale go to every destination row d = dst[t][j] with
 // 0 <= d < R (the bound is checked here: other entries name no row).  The 16
-// lanes of a quarter read the same destination list (one cache line).
+// lanes of a quarter read the same destination list (one cache line).  A
+// wavefront takes kScatterQuads x 4 groups: 2 measured 5% faster than 4 and
+// 9% faster than 1 on [1024, 7168] top-8.
+constexpr int kScatterQuads = 2;
 template <bool F16, int FMT>
 __global__ __launch_bounds__(256) void quant_g128_scatter_kernel(
     const uint16_t* __restrict__ x, int64_t T, int64_t G, int64_t ld_x,
@@ -217,11 +220,11 @@ __global__ __launch_bounds__(256) void quant_g128_scatter_kernel(
   const int l16 = lane & 15;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t total = T * G;
-  uint4 gv[kQuads];
-  int64_t tok[kQuads], grp[kQuads];
+  uint4 gv[kScatterQuads];
+  int64_t tok[kScatterQuads], grp[kScatterQuads];
 #pragma unroll
-  for (int u = 0; u < kQuads; ++u) {
-    const int64_t gid = (wave * kQuads + u) * 4 + quarter;
+  for (int u = 0; u < kScatterQuads; ++u) {
+    const int64_t gid = (wave * kScatterQuads + u) * 4 + quarter;
     tok[u] = -1;
     grp[u] = 0;
     gv[u] = make_uint4(0, 0, 0, 0);
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(256) void quant_g128_scatter_kernel(
     }
   }
 #pragma unroll
-  for (int u = 0; u < kQuads; ++u) {
+  for (int u = 0; u < kScatterQuads; ++u) {
     float y[8], sval;
     int eb;
     widen8<F16>(gv[u], y);
@@ -813,7 +816,7 @@ static hipError_t launch_g128(int fmt, const QuantArgs& a, hipStream_t s) {
 template <bool F16>
 static hipError_t launch_g128_scatter(int fmt, const ScatterArgs& a, hipStream_t s) {
   const int64_t G = a.K / 128;
-  const int64_t waves = (a.T * G + 15) / 16;
+  const int64_t waves = (a.T * G + 4 * kScatterQuads - 1) / (4 * kScatterQuads);
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   return with_fmt(fmt, [&](auto f) {
     constexpr int FMT = decltype(f)::value;
