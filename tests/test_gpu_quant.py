@@ -202,3 +202,41 @@ def test_per_token_quant_max_width():
         assert np.array_equal(q.cpu().numpy(), ref.codes)
         want = ref.ue8m0_byte if pow2 else ref.scale
         assert np.array_equal(s.cpu().numpy().reshape(-1), want.reshape(-1))
+
+
+def _boundary_rows(K, dtype):
+    """Rows whose group maxima sit on the UE8M0 exponent boundary: exactly
+    448 * 2^k and the next representable value of the input dtype below and
+    above it (448 -+ 2 in bf16, 448 -+ 1/4 in fp16, times 2^k) for k across
+    the dtype's normal range, plus a row below the 1e-10 absmax floor and a
+    zero row.  The rest of each row is small noise, so the maximum decides
+    the scale."""
+    r = inputs.rng(11)
+    u, ks = (2.0, range(-24, 25, 3)) if dtype == torch.bfloat16 else (0.25, range(-14, 8))
+    rows = []
+    for k in ks:
+        for d in (-u, 0.0, u):
+            v = (448.0 + d) * 2.0 ** k          # exact in fp64 and in the dtype
+            row = r.standard_normal(K).astype(F32) * F32(v / 64)
+            row[r.integers(0, K)] = F32(v) * (1 if r.random() < 0.5 else -1)
+            rows.append(row)
+    rows.append(np.full(K, 1e-12, dtype=F32))
+    rows.append(np.zeros(K, dtype=F32))
+    xt = inputs.to_dtype(np.stack(rows), dtype)
+    # the planted maxima survive the conversion exactly
+    got = np.abs(inputs.widen(xt)[:-2]).max(axis=1)
+    want = np.array([(448.0 + d) * 2.0 ** k for k in ks for d in (-u, 0.0, u)])
+    assert np.array_equal(got.astype(np.float64), want)
+    return xt
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_ue8m0_exponent_boundary(dtype):
+    # the kernels take e = ceil(log2 RN32(a/448)) from the bit fields of the
+    # group maximum a, without a divide, and skip the clamp to +-448; these
+    # rows put a on both sides of every carry the bit-field rule makes
+    x = _boundary_rows(1024, dtype)
+    _check(x, -1, fp8sm.SCALE_UE8M0_BYTE, 0, what="ue8m0 boundary per-token")
+    _check(x, 128, fp8sm.SCALE_UE8M0_BYTE, fp8sm.LAYOUT_ROW_MAJOR, what="ue8m0 boundary g128")
+    _check(x, 128, fp8sm.SCALE_UE8M0_BYTE, fp8sm.LAYOUT_MN_MAJOR, what="ue8m0 boundary g128 mn")
+    _check(x, 128, fp8sm.SCALE_UE8M0_FP32, fp8sm.LAYOUT_ROW_MAJOR, what="ue8m0 fp32 value g128")
