@@ -1082,7 +1082,7 @@ __global__ __launch_bounds__(64 * NWD) void gemm_decode_kernel(
       for (int i = 0; i < TMD; ++i)
 #pragma unroll
         for (int e = 0; e < EPW; ++e) mast[i][e] = mast[i][e] + part[b][i][w * EPW + e][lane];
-    __syncthreads();
+    if (r + NWD < nblk) __syncthreads();  // (uniform) the next round rewrites part
   }
   // accumulator element e of lane l is output row 32i + l % 32, column
   // 8 (e / 4) + 4 (l / 32) + e % 4; wavefront w stores its elements
