@@ -17,9 +17,23 @@ BUILD = os.path.join(ROOT, "_build")
 OBJS = [os.path.join(BUILD, n) for n in ("gemm.o", "quant.o", "probe.o")]
 RUNTIME = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
 
+CSRC = os.path.join(ROOT, "column_scaled_gemm_amd", "csrc")
+
+
+def _objects_current():
+    """Every device object exists and is newer than every kernel source and
+    header (a stale object could lack a symbol the current api.cpp needs)."""
+    if not all(os.path.exists(o) for o in OBJS):
+        return False
+    newest_src = max(os.path.getmtime(p) for p in glob.glob(os.path.join(CSRC, "*"))
+                     if p.endswith((".hip", ".h")))
+    return min(os.path.getmtime(o) for o in OBJS) >= newest_src
+
+
 pytestmark = pytest.mark.skipif(
-    not all(os.path.exists(o) for o in OBJS) or not RUNTIME,
-    reason="device objects (build first) or the sanitizer runtime missing")
+    not _objects_current() or not RUNTIME,
+    reason="device objects missing or older than the sources (build first), "
+           "or the sanitizer runtime missing")
 
 
 def _hipcc():
