@@ -726,6 +726,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
   const uint8_t* escb = reinterpret_cast<const uint8_t*>(esc);
   const float* sbrow = sbb + (int64_t)tn * nkb;
 
+  const bool live = m0 + wm * (BM / 2) < M;  // wavefront has a live row (uniform)
   const int a_off0 = wm * (BM / 2) * kChunk + frag32_off(lane, 0);
   const int a_off1 = wm * (BM / 2) * kChunk + frag32_off(lane, 1);
   const int b_off0 = (BM + wn * (BN / 2)) * kChunk + frag32_off(lane, 0);
@@ -791,19 +792,22 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
       fb[j].q[0] = *reinterpret_cast<const uint4*>(slot + b_off0 + j * 32 * kChunk);
       fb[j].q[1] = *reinterpret_cast<const uint4*>(slot + b_off1 + j * 32 * kChunk);
     }
-    mma32_chunk<TM, TN, true, decltype(fresh)::value>(fa, asc, fb, acc);
+    // a wavefront whose rows all lie past the live rows (a masked expert's
+    // few rows) neither multiplies nor promotes: none of its rows is stored
+    if (live) mma32_chunk<TM, TN, true, decltype(fresh)::value>(fa, asc, fb, acc);
   };
   // one K block (two chunks; the last block of a K tail may have one) per
   // iteration, then its partial is promoted into the fp64 master
   for (int kc = 0; kc < nkc; kc += 2) {
     chunk(kc, std::true_type{});
     if (kc + 1 < nkc) chunk(kc + 1, std::false_type{});
+    if (live)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mast[i][j][v] = fma((double)acc[i][j][v], sbk[i], mast[i][j][v]);
+          for (int v = 0; v < 16; ++v) mast[i][j][v] = fma((double)acc[i][j][v], sbk[i], mast[i][j][v]);
   }
 
 #pragma unroll
