@@ -57,8 +57,8 @@ def assert_within_tolerance(gpu_bits, res, K, what=""):
 
 
 def progress(msg):
-    """A progress line on stdout and in gpurun_out/progress.log (long full-size
-    checks print while they run, not only when they end)."""
+    """A progress line on stdout and appended to progress.log in the run-output
+    folder (long full-size checks print while they run, not only when they end)."""
     line = f"[{time.strftime('%H:%M:%S')}] {msg}"
     print(line, flush=True)
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
