@@ -44,8 +44,8 @@ PEAK_HBM = 8000.0           # GB/s
 # passes, scaled by a plain-copy calibration (FETCH_SIZE x2, WRITE_SIZE x1;
 # profiles/gemm_rowwise_qkv_traffic.md).  Valid only for the gemm.hip source
 # and kernel variant it was measured on; reported as null once either changes.
-TRAFFIC = {"gemm_src_sha256_prefix": "cdd5ab7e288f118e", "workload": "qkv",
-           "kernel": "tile128x128", "bytes": 3133.2e6 + 368.2e6}
+TRAFFIC = {"gemm_src_sha256_prefix": "cd3142395b89e366", "workload": "qkv",
+           "kernel": "tile128x128", "bytes": 3120.1e6 + 367.7e6}
 
 
 def measured_traffic(workload, variant):

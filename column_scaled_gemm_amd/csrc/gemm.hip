@@ -678,9 +678,12 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
   constexpr int SEGS = SLOT / 1024;
   constexpr int DPS = SEGS / 4;
   constexpr int SEGB = 64;  // K blocks of activation scale bytes staged at a time
+  // their row stride in LDS: 17 words, so the 32 rows a wavefront reads at
+  // once fall in distinct banks (a 16-word stride folded them onto a few)
+  constexpr int SEGP = SEGB + 4;
   static_assert(NSLOT >= 2 && NSLOT <= 4, "ring depth");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NSLOT * SLOT];
-  __shared__ __attribute__((aligned(16))) uint32_t esc[BM * SEGB / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t esc[BM * SEGP / 4];
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
@@ -720,7 +723,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
         const int kb = kb0 + half * 32 + 4 * q + b;
         v |= (uint32_t)(kb < nkb ? er[kb] : 127) << (8 * b);
       }
-      esc[(row * SEGB + half * 32 + 4 * q) / 4] = v;
+      esc[(row * SEGP + half * 32 + 4 * q) / 4] = v;
     }
   };
   const uint8_t* escb = reinterpret_cast<const uint8_t*>(esc);
@@ -773,7 +776,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_block_ue8m0_kernel(
       const double sb64 = (double)sbrow[kb];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int e = (int)escb[(wm * 64 + 32 * i + (lane & 31)) * SEGB + kb % SEGB] - 127;
+        const int e = (int)escb[(wm * 64 + 32 * i + (lane & 31)) * SEGP + kb % SEGB] - 127;
         const int ein = min(max(e, -kWidenExp), kWidenExp);
         asc[i] = __uint_as_float((uint32_t)(ein + 127) << 23);
         sbk[i] = __builtin_ldexp(sb64, e - ein);
